@@ -1,0 +1,192 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) weight-absorbed MLA decode library.
+ *
+ * Operation (web page "MLA deep compression", operatorworld.com, sections
+ * "Absorption: an equivalent rewrite at inference" and "Decoupled RoPE"; and
+ * "Attention-head anatomy: one cache, four wirings", romaanj.github.io, section 5):
+ * every query head i of a new token scores the shared per-token cache row
+ * [c_j (d_c values) | k^R_j (d_r values)] with its absorbed query q~_i = W^QK_i h
+ * (q_nope) and its rotated RoPE query q^R_i (q_pe):
+ *
+ *     s_ij = softmax_scale * (q~_i . c_j + q^R_i . k^R_j)
+ *     a_i  = softmax_j(s_ij)          over the visible tokens j
+ *     u_i  = sum_j a_ij c_j           (latent space, d_c values)
+ *     o_i  = W^UV_i u_i               (d_v values)
+ *     lse_i = ln sum_j exp(s_ij)
+ *
+ * With s_q new tokens per sequence (multi-token decode, GQLA abstract on
+ * chatpaper.ai: s_q = 1 and s_q = 2), query position q of sequence b sits at
+ * index L_b - s_q + q and sees tokens 0 .. L_b - s_q + q (causal within the new
+ * tokens, each new token sees itself; L_b counts the new tokens).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, except the
+ *    params pointer (host).  The library never allocates, frees or synchronizes:
+ *    work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *  - All validation happens on the host before any launch; a failed check returns
+ *    an error status and enqueues nothing.  Data that lives on the device
+ *    (seq_lens, block_table, positions) cannot be checked synchronously: see the
+ *    per-argument notes for what the kernels do with out-of-range values.
+ *  - Status codes, never exceptions or aborts, cross the ABI.
+ *  - Arrays are dense row-major with the shapes given; "elements" are of the
+ *    array's own dtype.
+ *  - The library keeps no state besides cached device attributes; calls on
+ *    different streams may overlap if their outputs and workspaces are disjoint.
+ */
+#ifndef MLA_DECODE_H_
+#define MLA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+#define MLA_SPLIT_UNIT 64 /* tokens per scheduling unit of the split rule */
+
+typedef enum {
+  MLA_DTYPE_F32 = 0,
+  MLA_DTYPE_BF16 = 1,
+  MLA_DTYPE_FP8_E4M3 = 2 /* OCP FP8 E4M3 "fn": bias 7, max 448, NaN = 0x7F/0xFF, no inf */
+} mla_dtype_t;
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,       /* a size, stride or shape combination is unsupported */
+  MLA_ERR_DTYPE = 3,       /* an unsupported dtype combination */
+  MLA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than mla_decode_workspace_size() */
+  MLA_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
+  MLA_ERR_UNSUPPORTED = 6  /* no kernel for this device */
+} mla_status_t;
+
+/*
+ * Shapes and options of one decode call.
+ *
+ * Supported combinations (q_dtype, kv_dtype, w_dtype, out_dtype):
+ *   (F32,  F32,       F32,  F32)   any d_c <= 1024, d_r <= 256, d_v <= 1024, n_h <= 1024
+ *   (BF16, BF16,      BF16, BF16)  d_c = 512, d_r = 64, d_v = 128, n_h a multiple of 16,
+ *   (BF16, FP8_E4M3,  BF16, BF16)  and s_q * n_h <= 128 or a multiple of 128
+ * batch >= 1, 1 <= s_q <= 16, page_size a positive multiple of 64.
+ */
+typedef struct {
+  int32_t batch;             /* B: sequences in the call */
+  int32_t s_q;               /* new query tokens per sequence */
+  int32_t n_h;               /* query heads */
+  int32_t d_c;               /* latent width (512 in DeepSeek-V2/V3) */
+  int32_t d_r;               /* decoupled-RoPE key/query width (64) */
+  int32_t d_v;               /* per-head output width (128) */
+  int32_t page_size;         /* P: tokens per cache page; a contiguous cache is one page per sequence */
+  int32_t num_pages;         /* pages in the pool; page ids outside [0, num_pages) are never read */
+  int32_t max_pages_per_seq; /* row stride of block_table */
+  int32_t num_splits;        /* G >= 1: shares of the batch's tokens (see the split rule); 0 = auto */
+  int64_t c_kv_stride;       /* elements between consecutive pool slots of c_kv (>= d_c) */
+  int64_t k_pe_stride;       /* elements between consecutive pool slots of k_pe (>= d_r) */
+  float softmax_scale;       /* applied to the sum of both dot products, e.g. 1/sqrt(d_h + d_r) */
+  mla_dtype_t q_dtype, kv_dtype, w_dtype, out_dtype;
+} mla_decode_params_t;
+
+/*
+ * Split rule (how one call is divided into partial attentions).
+ * Sequence b is cut into n_b = ceil(L_b / 64) units; the units of all sequences, in
+ * batch order, form one list of U = sum_b n_b units, cut into G = num_splits shares
+ * of ceil(U / G) consecutive units.  Share w meets sequence b in at most one piece
+ * (tokens [t0, t1), t0 a multiple of 64); that piece's partial is stored in slot
+ * w + b.  Each sequence therefore owns the consecutive slots [first_b, first_b +
+ * count_b) with count_b = number of shares its units fall in.
+ *
+ * Workspace layout (all offsets from the workspace base, each 256-byte aligned):
+ *   split_table  int32 [B][2]                     (first slot, count) per sequence; (0, 0) if L_b = 0
+ *   partial_lse  float [num_slots][s_q][n_h]      ln-sum-exp of the piece's scores; -inf if empty
+ *   partial_u    float [num_slots][s_q][n_h][d_c] u of the piece, normalized by its own softmax sum
+ * with num_slots = G + B.  Rows of a piece that see no token have lse = -inf and u = 0.
+ */
+
+/* Effective number of splits G for these params on the current device
+ * (num_splits when positive, else a choice that fills the GPU).  Returns <= 0 on
+ * invalid params or when no device is present. */
+int32_t mla_decode_num_splits(const mla_decode_params_t* params);
+
+/* Bytes of workspace mla_decode_fwd needs (0 on invalid params). */
+size_t mla_decode_workspace_size(const mla_decode_params_t* params);
+
+/*
+ * One decode step of absorbed MLA over a paged latent cache.
+ *
+ *  q_nope      [B, s_q, n_h, d_c]  q_dtype  absorbed content queries q~_i
+ *  q_pe        [B, s_q, n_h, d_r]  q_dtype  RoPE queries, already rotated
+ *  c_kv        pool of latents; slot s at c_kv + s * c_kv_stride (kv_dtype, d_c values)
+ *  k_pe        pool of RoPE keys; slot s at k_pe + s * k_pe_stride (kv_dtype, d_r values,
+ *              already rotated).  A packed cache row [c | k^R] is c_kv = row base,
+ *              k_pe = row base + d_c, both strides d_c + d_r.
+ *  kv_scale    [num_pages * page_size] float, per-slot dequantization scale when
+ *              kv_dtype = FP8_E4M3 (value = code * scale); must be NULL otherwise
+ *  block_table [B, max_pages_per_seq] int32: token t of sequence b lives in slot
+ *              block_table[b][t / P] * P + t % P.  Entries past the sequence's last
+ *              page are not read; a page id outside [0, num_pages) makes its
+ *              tokens invisible (never read).
+ *  seq_lens    [B] int32: L_b, tokens in the cache of sequence b including the s_q
+ *              new ones; values are clamped to [0, max_pages_per_seq * P].
+ *  w_uv        [n_h, d_v, d_c] w_dtype: per-head up-projection W^UV_i
+ *  out         [B, s_q, n_h, d_v] out_dtype, or NULL to stop after the partials
+ *  lse         [B, s_q, n_h] float (natural log), or NULL
+ *  workspace   device buffer of workspace_bytes >= mla_decode_workspace_size()
+ *
+ * A row with no visible token yields o = 0 and lse = -inf.  Results depend only on
+ * the logical token order, not on the page placement.
+ */
+mla_status_t mla_decode_fwd(const mla_decode_params_t* params, const void* q_nope, const void* q_pe,
+                            const void* c_kv, const void* k_pe, const float* kv_scale,
+                            const int32_t* block_table, const int32_t* seq_lens, const void* w_uv,
+                            void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Merge split partials and up-project: for every (b, q, head),
+ *   lse = ln sum_s exp(lse_s)  over the sequence's slots (skipping -inf),
+ *   u   = sum_s exp(lse_s - lse) u_s,   o = W^UV_i u.
+ * Reads split_table, partial_lse and partial_u from `workspace` (layout above),
+ * e.g. as left by mla_decode_fwd with out == NULL, or written by the caller.
+ * Slot ranges are clipped to [0, G + B); a sequence whose slots are all empty
+ * yields o = 0 and lse = -inf.
+ */
+mla_status_t mla_decode_splitkv_combine(const mla_decode_params_t* params, const void* workspace,
+                                        size_t workspace_bytes, const void* w_uv, void* out, float* lse,
+                                        void* stream);
+
+/*
+ * Append new cache rows (the write that precedes attention; page "MLA deep
+ * compression", low-rank projection and decoupled-RoPE sections: only c_t and
+ * k^R_t are cached).
+ *
+ *  c_new     [B, s_new, d_c] in_dtype,  k_pe_new [B, s_new, d_r] in_dtype
+ *  positions [B, s_new] int32 absolute token indices (distinct within a sequence)
+ *  c_kv, k_pe, kv_scale, block_table: the pool as in mla_decode_fwd (written in place)
+ *
+ * kv_dtype == in_dtype (F32 or BF16): the rows are copied bit for bit.
+ * kv_dtype == FP8_E4M3 (in_dtype F32 or BF16): each token's d_c + d_r values are
+ * quantized together: amax = max |x| (float32); amax = 0 gives scale = 1 and
+ * inv = 1, else inv = fp32(448 / amax) and scale = fp32(amax / 448);
+ * code = E4M3(fp32(x * inv)) rounded to nearest even, saturated to +-448;
+ * kv_scale[slot] = scale.
+ * A position whose page index is >= max_pages_per_seq, or whose page id is
+ * outside [0, num_pages), is skipped.  Uses params->batch, d_c, d_r, page_size,
+ * num_pages, max_pages_per_seq, strides and kv_dtype.
+ */
+mla_status_t mla_paged_cache_append(const mla_decode_params_t* params, const void* c_new,
+                                    const void* k_pe_new, int32_t s_new, mla_dtype_t in_dtype,
+                                    const int32_t* positions, const int32_t* block_table, void* c_kv,
+                                    void* k_pe, float* kv_scale, void* stream);
+
+/* Static description of a status code. */
+const char* mla_status_string(mla_status_t status);
+
+/* MLA_ABI_VERSION of the built library. */
+int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H_ */

@@ -1,0 +1,98 @@
+// Device-side building blocks for gfx950 (CDNA4): vector types, MFMA wrappers,
+// LDS transpose reads, direct global->LDS copies, wavefront reductions and the
+// OCP E4M3 conversions used by the MLA decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// C[16x16] += A[16x32] * B[32x16], bf16 inputs, fp32 accumulate.
+// Lane l holds A[l%16][8*(l/16) + j], B[8*(l/16) + j][l%16] (j = 0..7) and
+// C[4*(l/16) + i][l%16] (i = 0..3).
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed 8-byte LDS read: in each 16-lane block, lanes 4r..4r+3 give the
+// addresses of row r (4 x 4 consecutive 16-bit values = 16 columns); lane i of the
+// block receives column i of the 4 rows.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// 16-byte global -> LDS copy without a register round trip: lane l's 16 bytes land
+// at lds_wave_base + 16 * l (lds_wave_base must be wave-uniform).
+__device__ __forceinline__ void global_to_lds16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (MLA_LDS void*)(lds_wave_base), 16, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 concat4(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x2 pack_bf16(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_convertvector(v, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Two OCP E4M3 codes (bytes 0/1 or 2/3 of `packed`, selected by HI) -> two bf16,
+// exactly (every E4M3 value is representable in bf16).
+template <bool HI>
+__device__ __forceinline__ bf16x2 e4m3x2_to_bf16(unsigned packed) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, HI);
+}
+
+// float -> OCP E4M3 code, round to nearest even, saturating to +-448, NaN -> 0x7F.
+// Written from the format: 4 exponent bits (bias 7), 3 mantissa bits, subnormal
+// quantum 2^-9, largest finite 1.75 * 2^8.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7Fu;  // NaN
+  float a = __uint_as_float(u & 0x7FFFFFFFu);
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {                                   // below 2^-6: quantum 2^-9
+    uint32_t k = (uint32_t)__builtin_rintf(a * 512.0f);  // exact scaling, RNE; k = 8 is 2^-6
+    return sign | k;
+  }
+  int e = (int)((u >> 23) & 0xFFu) - 127;                // a in [2^e, 2^(e+1)), e in [-6, 8]
+  uint32_t k = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - e));  // 8..16
+  if (k == 16u) { e += 1; k = 8u; }
+  uint32_t code = ((uint32_t)(e + 7) << 3) | (k - 8u);
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+}  // namespace mla

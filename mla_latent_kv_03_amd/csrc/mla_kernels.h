@@ -1,0 +1,62 @@
+// Internal interface between the host dispatch (mla_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Arguments of the partial-attention kernels (one launch per decode call).
+struct AttnParams {
+  const void* q_nope;        // [B, s_q, n_h, d_c]
+  const void* q_pe;          // [B, s_q, n_h, d_r]
+  const void* c_kv;          // pool slot s at c_kv + s * c_stride (elements)
+  const void* k_pe;          // pool slot s at k_pe + s * k_stride
+  const float* kv_scale;     // per slot, fp8 caches only
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int64_t c_stride, k_stride;
+  int32_t batch, s_q, n_h, d_c, d_r;
+  int32_t page_size, num_pages, max_pages, max_tokens;
+  int32_t num_splits;        // G
+  int32_t rows_per_group;    // (q, head) rows per workgroup (MFMA path)
+  float scale_log2;          // softmax_scale * log2(e)
+  int32_t* split_table;      // [B][2]
+  float* part_lse;           // [G + B][s_q][n_h]
+  float* part_u;             // [G + B][s_q][n_h][d_c]
+};
+
+// Arguments of the combine + up-projection kernels.
+struct CombineParams {
+  const int32_t* split_table;
+  const float* part_lse;
+  const float* part_u;
+  const void* w_uv;          // [n_h, d_v, d_c]
+  void* out;                 // [B, s_q, n_h, d_v]
+  float* lse;                // [B, s_q, n_h] or null
+  int32_t batch, s_q, n_h, d_c, d_v;
+  int32_t num_slots;
+};
+
+struct AppendParams {
+  const void* c_new;         // [B, s_new, d_c]
+  const void* k_new;         // [B, s_new, d_r]
+  const int32_t* positions;  // [B, s_new]
+  const int32_t* block_table;
+  void* c_kv;
+  void* k_pe;
+  float* kv_scale;
+  int64_t c_stride, k_stride;
+  int32_t batch, s_new, d_c, d_r;
+  int32_t page_size, num_pages, max_pages;
+  int32_t in_f32;            // 1: float32 input, 0: bf16 input
+  int32_t mode;              // 0: copy bf16, 1: copy f32, 2: quantize to E4M3 + scale
+};
+
+hipError_t launch_attn_mfma(const AttnParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
+hipError_t launch_combine_bf16(const CombineParams& p, hipStream_t stream);
+hipError_t launch_combine_f32(const CombineParams& p, hipStream_t stream);
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,122 @@
+"""CPU tests of the C ABI: the library loads, exports what include/mla_decode.h
+declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+@pytest.fixture(scope="module")
+def b():
+    from mla_latent_kv_03_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for need in ("mla_decode_fwd", "mla_decode_splitkv_combine", "mla_paged_cache_append",
+                 "mla_decode_workspace_size", "mla_decode_num_splits", "mla_status_string", "mla_abi_version"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol(b):
+    lib = ctypes.CDLL(b.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert b.LIB.mla_abi_version() == 1
+
+
+def test_status_strings(b):
+    for code, name in b.STATUS.items():
+        assert b.lib_status_string(code).startswith(name)
+    assert "unknown" in b.lib_status_string(99)
+
+
+def v3(b, **kw):
+    args = dict(batch=4, s_q=1, n_h=128, d_c=512, d_r=64, d_v=128, page_size=64, num_pages=100,
+                max_pages_per_seq=32, c_kv_stride=576, k_pe_stride=576, softmax_scale=0.0722,
+                q_dtype=b.BF16, kv_dtype=b.BF16, num_splits=16)
+    args.update(kw)
+    return b.make_params(**args)
+
+
+def test_workspace_size_matches_header_layout(b):
+    p = v3(b, batch=5, s_q=2, num_splits=16)
+    a256 = lambda x: (x + 255) // 256 * 256
+    slots = 16 + 5
+    rows = slots * 2 * 128
+    assert b.mla_decode_workspace_size(p) == a256(5 * 8) + a256(rows * 4) + a256(rows * 512 * 4)
+    assert b.mla_decode_num_splits(p) == 16
+
+
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced: validation fails first
+
+
+def fwd(b, p, ws_bytes=1 << 40, **override):
+    ptrs = dict(q_nope=FAKE, q_pe=FAKE, c_kv=FAKE, k_pe=FAKE, kv_scale=None, block_table=FAKE, seq_lens=FAKE,
+                w_uv=FAKE, out=FAKE, lse=None, workspace=FAKE)
+    ptrs.update(override)
+    return b.LIB.mla_decode_fwd(ctypes.byref(p) if p is not None else None, ptrs["q_nope"], ptrs["q_pe"],
+                                ptrs["c_kv"], ptrs["k_pe"], ptrs["kv_scale"], ptrs["block_table"], ptrs["seq_lens"],
+                                ptrs["w_uv"], ptrs["out"], ptrs["lse"], ptrs["workspace"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(q_dtype=0), 3),                       # f32 queries with a bf16 cache
+    (dict(kv_dtype=0), 3),
+    (dict(d_c=256), 2), (dict(d_r=32), 2), (dict(d_v=64), 2),
+    (dict(n_h=24), 2),                          # not a multiple of 16
+    (dict(n_h=64, s_q=3), 2),                   # 192 rows: neither <= 128 nor a multiple of 128
+    (dict(page_size=32), 2), (dict(page_size=96), 2),
+    (dict(batch=0), 2), (dict(s_q=0), 2), (dict(s_q=17), 2),
+    (dict(c_kv_stride=500), 2),                 # shorter than d_c
+    (dict(c_kv_stride=580), 2),                 # rows not 16-byte aligned
+    (dict(num_splits=-1), 2),
+    (dict(softmax_scale=0.0), 2),
+])
+def test_fwd_rejects_bad_params(b, change, code):
+    assert fwd(b, v3(b, **change)) == code
+
+
+def test_fwd_rejects_null_and_workspace(b):
+    p = v3(b)
+    assert fwd(b, None) == 1
+    assert fwd(b, p, q_nope=None) == 1
+    assert fwd(b, p, seq_lens=None) == 1
+    assert fwd(b, p, kv_scale=FAKE) == 3                       # scale given for a bf16 cache
+    assert fwd(b, v3(b, kv_dtype=b.FP8)) == 1                  # fp8 cache without scales
+    assert fwd(b, p, q_nope=ctypes.c_void_p(0x10008)) == 2     # misaligned
+    need = b.mla_decode_workspace_size(p)
+    assert fwd(b, p, ws_bytes=need - 1) == 4
+    assert fwd(b, p, workspace=None) == 4
+
+
+def test_combine_and_append_validation(b):
+    p = v3(b)
+    lib = b.LIB
+    assert lib.mla_decode_splitkv_combine(ctypes.byref(p), FAKE, 10, FAKE, FAKE, None, None) == 4
+    assert lib.mla_decode_splitkv_combine(ctypes.byref(p), FAKE, 1 << 40, None, FAKE, None, None) == 1
+    ap = lambda params, in_dt, scale=None, s_new=3: lib.mla_paged_cache_append(
+        ctypes.byref(params), FAKE, FAKE, s_new, in_dt, FAKE, FAKE, FAKE, FAKE, scale, None)
+    assert ap(p, b.F32) == 3                                   # f32 rows into a bf16 cache
+    assert ap(v3(b, kv_dtype=b.FP8), b.BF16) == 1              # fp8 without scales
+    assert ap(p, b.BF16, scale=FAKE) == 3
+    assert ap(p, b.BF16, s_new=0) == 2
+    assert ap(v3(b, page_size=48), b.BF16) == 2
+
+
+def test_fp32_path_limits(b):
+    p = v3(b, q_dtype=b.F32, kv_dtype=b.F32, d_c=2048)
+    assert fwd(b, p) == 2
+    p = v3(b, q_dtype=b.F32, kv_dtype=b.F32, d_c=64, d_r=16, d_v=16, n_h=8)
+    assert fwd(b, p, ws_bytes=0) == 4
