@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of absorbed-MLA decode on one MI355X.
+
+One step = the whole hot path on one batch: append the new token's cache row
+(mla_paged_cache_append), partial attention over the latent cache, log-sum-exp
+combine and W^UV up-projection (mla_decode_fwd + mla_decode_splitkv_combine).
+Default workload: DeepSeek-V3 decode shape, batch 64, one query token, 4096-token
+contiguous bf16 latent caches (576 values per token), seeded synthetic inputs.
+
+Prints one JSON line.  value = cached tokens processed per second (sum of the
+sequence lengths per step / wall time per step).  The "roofline" object reports the
+dominant kernel (partial attention): algorithmic HBM bytes per launch / its average
+duration measured with HIP events on the launch stream.  Inputs stay resident in
+HBM; steps rotate over several copies of them so that the 256 MB Infinity Cache
+cannot serve a step from the previous one.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode latent-KV tokens/s + achieved HBM GB/s & MFMA % of peak"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_partial_traffic.json")
+
+WORKLOADS = ("v3_decode_b64_l4096", "v3_paged_b128", "v3_mtp_b32_l32768", "v3_long_fp8_b4_l131072")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=WORKLOADS[0], choices=WORKLOADS)
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate-bytes", type=float, default=1.0e9,
+                    help="total bytes of rotating input copies (cold Infinity Cache per step)")
+    return ap.parse_args()
+
+
+def make_workload(name):
+    from mla_latent_kv_03_amd import workloads
+    return {"v3_decode_b64_l4096": workloads.v3_decode, "v3_paged_b128": workloads.v3_paged,
+            "v3_mtp_b32_l32768": workloads.v3_mtp, "v3_long_fp8_b4_l131072": workloads.v3_long_fp8}[name]()
+
+
+class Resident:
+    """One copy of a decode call's inputs in HBM, plus the tensors one step writes."""
+
+    def __init__(self, x, binding, num_splits, dev):
+        import torch
+        self.x = x
+        self.q_nope, self.q_pe = x.q_nope.to(dev), x.q_pe.to(dev)
+        self.block_table, self.seq_lens = x.block_table.to(dev), x.seq_lens.to(dev)
+        self.w_uv = x.w_uv.to(dev)
+        d_c = x.d_c
+        lens = x.seq_lens.numpy()
+        tab = x.block_table.numpy()
+        # the new token of each sequence is its last cached row: position L_b - 1
+        last = [int(L) - 1 for L in lens]
+        self.positions = torch.tensor(last, dtype=torch.int32, device=dev)[:, None].contiguous()
+        last_slots = [int(tab[b, p // x.page_size]) * x.page_size + p % x.page_size for b, p in enumerate(last)]
+        new_rows = x.pool[torch.tensor(last_slots)]
+        self.kv_scale = None
+        if x.kv_dtype == "fp8":
+            self.pool = torch.zeros(x.pool.shape, dtype=torch.uint8, device=dev)
+            self.kv_scale = torch.zeros(x.pool.shape[0], dtype=torch.float32, device=dev)
+            qp = binding.make_params(batch=1, s_q=1, n_h=x.n_h, d_c=d_c, d_r=x.d_r, d_v=x.d_v, page_size=x.page_size,
+                                     num_pages=x.num_pages, max_pages_per_seq=tab.shape[1], c_kv_stride=x.pool.shape[1],
+                                     k_pe_stride=x.pool.shape[1], softmax_scale=x.softmax_scale, q_dtype=binding.BF16,
+                                     kv_dtype=binding.FP8)
+            for b in range(x.batch):
+                j = torch.arange(int(lens[b]))
+                slots = torch.from_numpy(tab[b])[j // x.page_size].long() * x.page_size + j % x.page_size
+                src = x.pool[slots].to(dev)[None]
+                binding.mla_paged_cache_append(qp, src[..., :d_c].contiguous(), src[..., d_c:].contiguous(),
+                                               torch.arange(int(lens[b]), dtype=torch.int32, device=dev)[None],
+                                               self.block_table[b:b + 1], self.pool[:, :d_c], self.pool[:, d_c:],
+                                               self.kv_scale)
+            self.new_c = new_rows[:, None, :d_c].to(dev).contiguous()             # float32 source rows
+            self.new_k = new_rows[:, None, d_c:].to(dev).contiguous()
+        else:
+            self.pool = x.pool.to(dev)
+            self.new_c = new_rows[:, None, :d_c].to(dev).contiguous()
+            self.new_k = new_rows[:, None, d_c:].to(dev).contiguous()
+        self.c_kv, self.k_pe = self.pool[:, :d_c], self.pool[:, d_c:]
+        self.params = binding.params_for(self.q_nope, self.q_pe, self.c_kv, self.k_pe, self.block_table, self.w_uv,
+                                         softmax_scale=x.softmax_scale, page_size=x.page_size, num_splits=num_splits)
+        self.workspace = binding.alloc_workspace(self.params, dev)
+        self.out = torch.empty(x.q_nope.shape[:3] + (x.d_v,), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(x.q_nope.shape[:3], dtype=torch.float32, device=dev)
+
+    def prepare(self, binding):
+        """Marshal each entry point's arguments once, so a step is three plain C calls."""
+        import ctypes
+        import torch
+        P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.lib = binding.LIB
+        self.append_args = (ctypes.byref(self.params), P(self.new_c), P(self.new_k), 1,
+                            binding._DTYPE_CODE[self.new_c.dtype], P(self.positions), P(self.block_table),
+                            P(self.c_kv), P(self.k_pe), P(self.kv_scale), stream)
+        self.fwd_args = (ctypes.byref(self.params), P(self.q_nope), P(self.q_pe), P(self.c_kv), P(self.k_pe),
+                         P(self.kv_scale), P(self.block_table), P(self.seq_lens), P(self.w_uv), None, None,
+                         P(self.workspace), self.workspace.numel(), stream)
+        self.comb_args = (ctypes.byref(self.params), P(self.workspace), self.workspace.numel(), P(self.w_uv),
+                          P(self.out), P(self.lse), stream)
+
+    def nbytes(self):
+        return sum(t.numel() * t.element_size() for t in (self.pool, self.q_nope, self.q_pe, self.workspace))
+
+
+def step(r, ev=None):
+    if ev is not None:
+        ev[0].record()
+    rc = r.lib.mla_paged_cache_append(*r.append_args)
+    if ev is not None:
+        ev[1].record()
+    rc |= r.lib.mla_decode_fwd(*r.fwd_args)                 # out = NULL: partial attention only
+    if ev is not None:
+        ev[2].record()
+    rc |= r.lib.mla_decode_splitkv_combine(*r.comb_args)
+    if ev is not None:
+        ev[3].record()
+    if rc:
+        raise RuntimeError(f"library call failed with status {rc}")
+
+
+def algorithmic(x):
+    """Per-call algorithmic bytes and flops (one cached token = 576 values read once)."""
+    tokens = int(x.seq_lens.sum())
+    per_tok_bytes = 576 * (1 if x.kv_dtype == "fp8" else 2) + (4 if x.kv_dtype == "fp8" else 0)
+    q_bytes = x.batch * x.s_q * x.n_h * (x.d_c + x.d_r) * 2
+    attn_bytes = tokens * per_tok_bytes + q_bytes
+    # visible tokens per query row: L - s_q + q + 1
+    vis = sum(max(0, int(L) - x.s_q + q + 1) for L in x.seq_lens.tolist() for q in range(x.s_q))
+    attn_flops = vis * x.n_h * 2 * (x.d_c + x.d_r + x.d_c)
+    up_flops = x.batch * x.s_q * x.n_h * x.d_v * x.d_c * 2
+    w_bytes = x.n_h * x.d_v * x.d_c * 2
+    return dict(tokens=tokens, attn_bytes=attn_bytes, attn_flops=attn_flops, total_bytes=attn_bytes + w_bytes,
+                total_flops=attn_flops + up_flops)
+
+
+def cpu_baseline(x, budget_s=12.0):
+    """The float64 oracle on host cores over a bounded sample of the same workload."""
+    import numpy as np
+    from oracle import mla_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    qn = x.q_nope.double().numpy()
+    qp = x.q_pe.double().numpy()
+    w = x.w_uv.double().numpy()
+    tab = x.block_table.numpy()
+    done_tokens, spent, seqs = 0, 0.0, 0
+    for b in range(x.batch):
+        L = int(x.seq_lens[b])
+        j = np.arange(L)
+        slots = tab[b, j // x.page_size].astype(np.int64) * x.page_size + j % x.page_size
+        rows = x.pool[slots].double().numpy()
+        if x.kv_dtype == "fp8":
+            from oracle import fp8
+            codes, sc = fp8.quantize_rows(rows.astype(np.float32))
+            rows = fp8.e4m3_decode_table()[codes] * sc.astype(np.float64)[:, None]
+        t0 = time.perf_counter()
+        for q in range(x.s_q):
+            ref.mla_absorbed(qn[b, q], qp[b, q], rows[:, :x.d_c], rows[:, x.d_c:], w, x.softmax_scale,
+                             ref.visible_len(L, x.s_q, q))
+        spent += time.perf_counter() - t0
+        done_tokens += L
+        seqs += 1
+        if spent >= budget_s:
+            break
+    return {"value": done_tokens / spent, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{seqs} of {x.batch} sequences ({done_tokens} cached tokens, s_q={x.s_q}), float64 NumPy, "
+                      f"{spent:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mla_latent_kv_03_amd import binding
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    print(f"[bench] workload {args.workload}: generating inputs", file=sys.stderr, flush=True)
+    x = make_workload(args.workload)
+    first = Resident(x, binding, args.num_splits, dev)
+    copies = [first]
+    n_copies = max(2, min(8, math.ceil(args.rotate_bytes / max(1, first.nbytes())) + 1))
+    for _ in range(n_copies - 1):
+        copies.append(Resident(x, binding, args.num_splits, dev))
+    for r in copies:
+        r.prepare(binding)
+    G = binding.mla_decode_num_splits(first.params)
+    print(f"[bench] {n_copies} resident copies of {first.nbytes() / 1e6:.1f} MB, G={G}", file=sys.stderr, flush=True)
+
+    for i in range(args.warmup):
+        step(copies[i % n_copies])
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(copies[i % n_copies], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    comb_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    app_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step; append {app_ms * 1e3:.1f} us, "
+          f"attention {attn_ms * 1e3:.1f} us, combine {comb_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    alg = algorithmic(x)
+    attn_gbs = alg["attn_bytes"] / (attn_ms * 1e-3) / 1e9
+    attn_tflops = alg["attn_flops"] / (attn_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE)).get(args.workload)
+        if rec:
+            traffic = rec.get("bytes_per_launch")
+    roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "attn_partial_mfma", "kernel_us": round(attn_ms * 1e3, 2),
+            "mfma_tflops": round(attn_tflops, 1), "mfma_frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
+            "algorithmic_bytes_per_launch": alg["attn_bytes"], "algorithmic_flops_per_launch": alg["attn_flops"]}
+    result = {
+        "metric": METRIC, "value": round(alg["tokens"] / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if x.kv_dtype == "bf16" else "bf16+fp8e4m3",
+        "data": "synthetic (seeded N(0,1) queries and cache, N(0,1/512) W^UV; no trained weights)",
+        "config": {"workload": args.workload, "batch": x.batch, "s_q": x.s_q, "n_h": x.n_h, "d_c": x.d_c,
+                   "d_r": x.d_r, "d_v": x.d_v, "context": int(x.seq_lens.max()),
+                   "cached_tokens_per_step": alg["tokens"], "kv_dtype": x.kv_dtype, "page_size": x.page_size,
+                   "num_splits": G, "step": "append + partial attention + combine/up-projection",
+                   "hbm_gbs_whole_step": round(alg["total_bytes"] / (ms_step * 1e-3) / 1e9, 1)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

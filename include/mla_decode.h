@@ -67,8 +67,9 @@ typedef enum {
  *
  * Supported combinations (q_dtype, kv_dtype, w_dtype, out_dtype):
  *   (F32,  F32,       F32,  F32)   any d_c <= 1024, d_r <= 256, d_v <= 1024, n_h <= 1024
- *   (BF16, BF16,      BF16, BF16)  d_c = 512, d_r = 64, d_v = 128, n_h a multiple of 16,
- *   (BF16, FP8_E4M3,  BF16, BF16)  and s_q * n_h <= 128 or a multiple of 128
+ *   (BF16, BF16,      BF16, BF16)  d_c = 512, d_r = 64, d_v = 128, n_h = 16, 32 or a multiple of 64
+ *   (BF16, FP8_E4M3,  BF16, BF16)  d_c = 512, d_r = 64, d_v = 128, n_h a multiple of 16 and
+ *                                  s_q * n_h <= 128 or a multiple of 128
  * batch >= 1, 1 <= s_q <= 16, page_size a positive multiple of 64.
  */
 typedef struct {

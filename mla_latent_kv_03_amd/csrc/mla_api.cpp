@@ -44,8 +44,9 @@ Path path_of(const mla_decode_params_t& p) {
   return Path::kNone;
 }
 
-// Rows of (query position, head) handled by one workgroup on the MFMA path.
+// Rows of (query position, head) handled by one workgroup on the MFMA paths.
 int rows_per_group(const mla_decode_params_t& p) {
+  if (path_of(p) == Path::kBf16) return mla::attn_heads_per_group(p.n_h);
   const int rows = p.s_q * p.n_h;
   return rows <= 128 ? rows : 128;
 }
@@ -71,8 +72,12 @@ mla_status_t check_common(const mla_decode_params_t* p) {
     case Path::kFp8: {
       if (p->d_c != 512 || p->d_r != 64 || p->d_v != 128) return MLA_ERR_SHAPE;
       if (p->n_h % 16 != 0) return MLA_ERR_SHAPE;
-      const int rows = p->s_q * p->n_h;
-      if (rows > 128 && rows % 128 != 0) return MLA_ERR_SHAPE;
+      if (path_of(*p) == Path::kBf16) {
+        if (!(p->n_h == 16 || p->n_h == 32 || p->n_h % 64 == 0)) return MLA_ERR_SHAPE;
+      } else {
+        const int rows = p->s_q * p->n_h;
+        if (rows > 128 && rows % 128 != 0) return MLA_ERR_SHAPE;
+      }
       const int align = path_of(*p) == Path::kFp8 ? 16 : 8;  // 16-byte rows for the tile copies
       if (p->c_kv_stride % align != 0 || p->k_pe_stride % align != 0) return MLA_ERR_SHAPE;
       break;
@@ -91,7 +96,8 @@ int resolve_splits(const mla_decode_params_t& p) {
     return g < 1 ? 1 : (g > 64 ? 64 : g);
   }
   const int groups = (p.s_q * p.n_h) / rows_per_group(p);
-  const int g = cus / groups;
+  int g = cus / groups;
+  if (g >= 16) g -= g % 8;   // all row groups of a share then sit on one XCD (shared L2)
   return g < 1 ? 1 : g;
 }
 
@@ -209,6 +215,10 @@ mla_status_t mla_decode_fwd(const mla_decode_params_t* params, const void* q_nop
   a.max_tokens = p.max_pages_per_seq * p.page_size;
   a.num_splits = G;
   a.rows_per_group = rows_per_group(p);
+  {
+    const size_t elem = path == Path::kF32 ? 4 : (path == Path::kFp8 ? 1 : 2);
+    a.packed_rows = (k_pe == (const char*)c_kv + (size_t)p.d_c * elem && p.c_kv_stride == p.k_pe_stride) ? 1 : 0;
+  }
   a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
   a.split_table = (int32_t*)((char*)workspace + l.table);
   a.part_lse = (float*)((char*)workspace + l.lse);

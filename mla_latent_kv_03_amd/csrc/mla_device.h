@@ -37,10 +37,15 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// Cache-policy bit "nt" (non-temporal) of gfx950 vector memory instructions.  For
+// data streamed once it roughly doubles the HBM read rate of direct-to-LDS copies
+// (measured on MI355X: about 3.9 -> 6.9 TB/s).
+constexpr int kCachePolicyNT = 2;
+
 // 16-byte global -> LDS copy without a register round trip: lane l's 16 bytes land
-// at lds_wave_base + 16 * l (lds_wave_base must be wave-uniform).
+// at lds_wave_base + 16 * l (lds_wave_base must be wave-uniform).  Streaming policy.
 __device__ __forceinline__ void global_to_lds16(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (MLA_LDS void*)(lds_wave_base), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(gsrc, (MLA_LDS void*)(lds_wave_base), 16, 0, kCachePolicyNT);
 }
 
 __device__ __forceinline__ bf16x8 concat4(bf16x4 a, bf16x4 b) {
@@ -55,6 +60,26 @@ __device__ __forceinline__ bf16x2 pack_bf16(float a, float b) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Reductions across the four 16-lane rows of a wave with gfx950's row-swapping
+// permutes (no LDS round trip).  permlane16_swap(v, v) yields rows (0,0,2,2) and
+// (1,1,3,3); permlane32_swap(v, v) yields halves (lo,lo) and (hi,hi).
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

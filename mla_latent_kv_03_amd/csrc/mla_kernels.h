@@ -20,6 +20,7 @@ struct AttnParams {
   int32_t page_size, num_pages, max_pages, max_tokens;
   int32_t num_splits;        // G
   int32_t rows_per_group;    // (q, head) rows per workgroup (MFMA path)
+  int32_t packed_rows;       // 1: k_pe == c_kv + d_c with equal strides (one [c | k_pe] row per slot)
   float scale_log2;          // softmax_scale * log2(e)
   int32_t* split_table;      // [B][2]
   float* part_lse;           // [G + B][s_q][n_h]
@@ -53,7 +54,10 @@ struct AppendParams {
   int32_t mode;              // 0: copy bf16, 1: copy f32, 2: quantize to E4M3 + scale
 };
 
+// Heads of one query position handled by one workgroup of the bf16 kernel.
+int attn_heads_per_group(int n_h);
 hipError_t launch_attn_mfma(const AttnParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_attn_fp8_v0(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
 hipError_t launch_combine_bf16(const CombineParams& p, hipStream_t stream);
 hipError_t launch_combine_f32(const CombineParams& p, hipStream_t stream);

@@ -116,4 +116,116 @@ __device__ void for_each_piece(const int32_t* __restrict__ seq_lens, int B, int 
   }
 }
 
+__device__ __forceinline__ long long wave_inclusive_scan(long long x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const long long y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ long long wave_total(long long x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+  return x;
+}
+
+// Same walk as for_each_piece, done by each wave on its own (64 sequences per step,
+// wave-level scans, no LDS and no barriers): every wave of a workgroup derives the
+// identical piece list and calls process(piece) in the same order with wave-uniform
+// values.  The wave given a non-null `table` also writes the split-table entries of
+// the sequences b with b % G == w.
+template <class F>
+__device__ void for_each_piece_wave(const int32_t* __restrict__ seq_lens, int B, int max_tokens, int G, int w,
+                                    int32_t* __restrict__ table, F&& process) {
+  const int lane = threadIdx.x & 63;
+  long long total = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    total += wave_total(b < B ? (clamp_len(seq_lens[b], max_tokens) + kSplitUnit - 1) / kSplitUnit : 0);
+  }
+  if (total == 0) {
+    if (table)
+      for (int b = lane; b < B; b += 64)
+        if (b % G == w) { table[2 * b] = 0; table[2 * b + 1] = 0; }
+    return;
+  }
+  const long long share = (total + G - 1) / G;
+  const long long lo = (long long)w * share;
+  const long long hi = lo + share < total ? lo + share : total;
+  long long carry = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    const int L = b < B ? clamp_len(seq_lens[b], max_tokens) : 0;
+    const long long n = (L + kSplitUnit - 1) / kSplitUnit;
+    const long long incl = wave_inclusive_scan(n);
+    const long long start = carry + incl - n;
+    if (table && b < B && b % G == w) {
+      int first = 0, cnt = 0;
+      if (n > 0) {
+        const long long wf = start / share, wl = (start + n - 1) / share;
+        first = (int)wf + b;
+        cnt = (int)(wl - wf + 1);
+      }
+      table[2 * b] = first;
+      table[2 * b + 1] = cnt;
+    }
+    const bool mine = n > 0 && start < hi && start + n > lo;
+    const long long u0 = (lo > start ? lo : start) - start;
+    const long long u1 = (hi < start + n ? hi : start + n) - start;
+    const int t0 = (int)(u0 * kSplitUnit);
+    const int t1 = (int)(u1 * kSplitUnit < L ? u1 * kSplitUnit : L);
+    unsigned long long mask = __ballot(mine);
+    while (mask) {
+      const int src = __builtin_ctzll(mask);
+      mask &= mask - 1;
+      Piece pc;
+      pc.b = __builtin_amdgcn_readlane(b, src);
+      pc.t0 = __builtin_amdgcn_readlane(t0, src);
+      pc.t1 = __builtin_amdgcn_readlane(t1, src);
+      pc.slot = w + pc.b;
+      process(pc);
+    }
+    carry += __shfl(incl, 63, 64);
+    if (!table && carry >= hi) break;
+  }
+}
+
+// Block-table entries of one sequence held in registers: lane j of the wave keeps the
+// page id of logical page base + j (or -1 when that id is outside [0, num_pages) or
+// past the table row), so looking a page up is a register read instead of a memory
+// round trip.  The window slides forward (one coalesced load) when a lookup passes
+// its end; lookups must not go back more than 32 pages behind the furthest one.
+struct PageWindow {
+  const int32_t* row;   // block_table + b * max_pages
+  int max_pages, num_pages;
+  int base;
+  int ids;              // this lane's page id
+
+  __device__ void load(int new_base) {
+    base = new_base;
+    const int lane = threadIdx.x & 63;
+    const int k = base + lane;
+    int id = -1;
+    if (k < max_pages) {
+      id = row[k];
+      if (id < 0 || id >= num_pages) id = -1;
+    }
+    ids = id;
+  }
+  __device__ void init(const int32_t* row_, int max_pages_, int num_pages_, int first_page) {
+    row = row_;
+    max_pages = max_pages_;
+    num_pages = num_pages_;
+    load(first_page);
+  }
+  // page id of logical page `page_idx` (wave-uniform), -1 if invalid
+  __device__ int get(int page_idx) {
+    if (page_idx >= base + 64) load(page_idx - 32 > base ? page_idx - 32 : base + 32);
+    return __builtin_amdgcn_readlane(ids, page_idx - base);
+  }
+};
+
 }  // namespace mla

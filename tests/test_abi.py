@@ -76,7 +76,8 @@ def fwd(b, p, ws_bytes=1 << 40, **override):
     (dict(kv_dtype=0), 3),
     (dict(d_c=256), 2), (dict(d_r=32), 2), (dict(d_v=64), 2),
     (dict(n_h=24), 2),                          # not a multiple of 16
-    (dict(n_h=64, s_q=3), 2),                   # 192 rows: neither <= 128 nor a multiple of 128
+    (dict(n_h=48), 2),                          # bf16 cache: n_h must be 16, 32 or a multiple of 64
+    (dict(n_h=64, s_q=3, kv_dtype=2), 2),       # E4M3 cache: 192 rows, neither <= 128 nor a multiple of 128
     (dict(page_size=32), 2), (dict(page_size=96), 2),
     (dict(batch=0), 2), (dict(s_q=0), 2), (dict(s_q=17), 2),
     (dict(c_kv_stride=500), 2),                 # shorter than d_c
