@@ -28,6 +28,7 @@ METRIC = "MLA decode latent-KV tokens/s + achieved HBM GB/s & MFMA % of peak"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_partial_traffic.json")
+ATTN_KERNEL = {"bf16": "attn_partial_split", "fp8": "attn_partial_mfma (E4M3 cache)"}
 
 WORKLOADS = ("v3_decode_b64_l4096", "v3_paged_b128", "v3_mtp_b32_l32768", "v3_long_fp8_b4_l131072")
 
@@ -42,6 +43,15 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-bytes", type=float, default=1.0e9,
                     help="total bytes of rotating input copies (cold Infinity Cache per step)")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="before the timed steps, run a plain streaming kernel (elementwise negation: reads and "
+                         "writes this many MiB) three times, so that a counter run (rocprofv3 --pmc FETCH_SIZE / "
+                         "WRITE_SIZE) sees a kernel of known traffic")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="RESULTS_DB",
+                    help="no GPU run: read rocprofv3 counter databases of a bench run made with "
+                         "--copy-calibration-mb, print the attention kernel's HBM traffic per launch and record "
+                         "it in profiles/attn_partial_traffic.json")
+    ap.add_argument("--pmc-command", default="", help="command line recorded with --pmc-summary")
     return ap.parse_args()
 
 
@@ -149,7 +159,9 @@ def algorithmic(x):
 
 
 def cpu_baseline(x, budget_s=12.0):
-    """The float64 oracle on host cores over a bounded sample of the same workload."""
+    """The float64 oracle on host cores over a bounded sample of the same workload: whole
+    sequences in batch order (repeating the batch if it is short) until about budget_s
+    seconds of oracle time."""
     import numpy as np
     from oracle import mla_ref as ref
     try:
@@ -161,32 +173,86 @@ def cpu_baseline(x, budget_s=12.0):
     qp = x.q_pe.double().numpy()
     w = x.w_uv.double().numpy()
     tab = x.block_table.numpy()
-    done_tokens, spent, seqs = 0, 0.0, 0
-    for b in range(x.batch):
-        L = int(x.seq_lens[b])
-        j = np.arange(L)
-        slots = tab[b, j // x.page_size].astype(np.int64) * x.page_size + j % x.page_size
-        rows = x.pool[slots].double().numpy()
-        if x.kv_dtype == "fp8":
-            from oracle import fp8
-            codes, sc = fp8.quantize_rows(rows.astype(np.float32))
-            rows = fp8.e4m3_decode_table()[codes] * sc.astype(np.float64)[:, None]
-        t0 = time.perf_counter()
-        for q in range(x.s_q):
-            ref.mla_absorbed(qn[b, q], qp[b, q], rows[:, :x.d_c], rows[:, x.d_c:], w, x.softmax_scale,
-                             ref.visible_len(L, x.s_q, q))
-        spent += time.perf_counter() - t0
-        done_tokens += L
-        seqs += 1
-        if spent >= budget_s:
-            break
+    done_tokens, spent, seqs, passes = 0, 0.0, 0, 0
+    rows_cache = {}
+    while spent < budget_s:
+        for b in range(x.batch):
+            L = int(x.seq_lens[b])
+            if b not in rows_cache:
+                j = np.arange(L)
+                slots = tab[b, j // x.page_size].astype(np.int64) * x.page_size + j % x.page_size
+                rows = x.pool[slots].double().numpy()
+                if x.kv_dtype == "fp8":
+                    from oracle import fp8
+                    codes, sc = fp8.quantize_rows(rows.astype(np.float32))
+                    rows = fp8.e4m3_decode_table()[codes] * sc.astype(np.float64)[:, None]
+                rows_cache[b] = rows if L * 576 * 8 < 2 ** 30 else None
+            else:
+                rows = rows_cache[b]
+            t0 = time.perf_counter()
+            for q in range(x.s_q):
+                ref.mla_absorbed(qn[b, q], qp[b, q], rows[:, :x.d_c], rows[:, x.d_c:], w, x.softmax_scale,
+                                 ref.visible_len(L, x.s_q, q))
+            spent += time.perf_counter() - t0
+            done_tokens += L
+            seqs += 1
+            if rows_cache.get(b) is None:
+                rows_cache.pop(b, None)
+            if spent >= budget_s:
+                break
+        passes += 1
     return {"value": done_tokens / spent, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{seqs} of {x.batch} sequences ({done_tokens} cached tokens, s_q={x.s_q}), float64 NumPy, "
-                      f"{spent:.1f} s"}
+            "sample": f"{seqs} sequences of {x.batch} in batch order ({done_tokens} cached tokens, s_q={x.s_q}, "
+                      f"{passes} pass(es) over the batch), float64 NumPy absorbed-form oracle, {spent:.1f} s"}
+
+
+def pmc_summary(args):
+    """Attention-kernel HBM traffic from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by the
+    ratio the same counter shows for the plain copy kernel of known size in the same run."""
+    import sqlite3
+    vals = {}   # (kernel kind, counter) -> per-dispatch totals
+    for path in args.pmc_summary:
+        db = sqlite3.connect(path)
+        cols = [r[1] for r in db.execute("pragma table_info(counters_collection)")]
+        ci = {c: i for i, c in enumerate(cols)}
+        per = {}
+        for r in db.execute("select * from counters_collection"):
+            name, ctr = r[ci["kernel_name"]], r[ci["counter_name"]]
+            kind = "attn" if "attn_partial" in name else ("copy" if "neg_kernel" in name else None)
+            if kind is None or ctr not in ("FETCH_SIZE", "WRITE_SIZE"):
+                continue
+            key = (kind, ctr, path, r[ci["dispatch_id"]])
+            per[key] = per.get(key, 0.0) + float(r[ci["value"]])
+        for (kind, ctr, _, _), v in per.items():
+            vals.setdefault((kind, ctr), []).append(v)
+    need = [("attn", "FETCH_SIZE"), ("attn", "WRITE_SIZE"), ("copy", "FETCH_SIZE"), ("copy", "WRITE_SIZE")]
+    missing = [k for k in need if k not in vals]
+    if missing:
+        raise SystemExit(f"counter data missing for {missing}")
+    mean = {k: sum(v) / len(v) for k, v in vals.items()}
+    copy_bytes = args.copy_calibration_mb * 2 ** 20
+    f_read = mean[("copy", "FETCH_SIZE")] * 1024 / copy_bytes
+    f_write = mean[("copy", "WRITE_SIZE")] * 1024 / copy_bytes
+    fetch = mean[("attn", "FETCH_SIZE")] * 1024 / f_read
+    write = mean[("attn", "WRITE_SIZE")] * 1024 / f_write
+    rec = {"bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch), "write_bytes": round(write),
+           "copy_factor_fetch": round(f_read, 4), "copy_factor_write": round(f_write, 4),
+           "attn_dispatches": len(vals[("attn", "FETCH_SIZE")]), "command": args.pmc_command}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    data = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    data[args.workload] = rec
+    json.dump(data, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
+    print(f"workload {args.workload}: attention kernel HBM traffic per launch {rec['bytes_per_launch'] / 1e6:.1f} MB "
+          f"(fetch {fetch / 1e6:.1f} MB, write {write / 1e6:.1f} MB); copy calibration: FETCH_SIZE reads "
+          f"{f_read:.4f}x and WRITE_SIZE {f_write:.4f}x the {args.copy_calibration_mb} MiB copied; "
+          f"{rec['attn_dispatches']} attention dispatches")
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -211,6 +277,15 @@ def main():
     for i in range(args.warmup):
         step(copies[i % n_copies])
     torch.cuda.synchronize()
+    if args.copy_calibration_mb:
+        # a plain streaming kernel of known traffic (reads and writes n bytes): torch's negation
+        n = args.copy_calibration_mb * 2 ** 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -236,7 +311,7 @@ def main():
             traffic = rec.get("bytes_per_launch")
     roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "attn_partial_mfma", "kernel_us": round(attn_ms * 1e3, 2),
+            "kernel": ATTN_KERNEL[x.kv_dtype], "kernel_us": round(attn_ms * 1e3, 2),
             "mfma_tflops": round(attn_tflops, 1), "mfma_frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
             "algorithmic_bytes_per_launch": alg["attn_bytes"], "algorithmic_flops_per_launch": alg["attn_flops"]}
     result = {
