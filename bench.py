@@ -28,7 +28,25 @@ METRIC = "MLA decode latent-KV tokens/s + achieved HBM GB/s & MFMA % of peak"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_partial_traffic.json")
-ATTN_KERNEL = {"bf16": "attn_partial_split", "fp8": "attn_partial_mfma (E4M3 cache)"}
+CSRC = os.path.join(ROOT, "mla_latent_kv_03_amd", "csrc")
+
+
+def attn_kernel(x):
+    """(kernel name, source files) of the partial-attention kernel the library runs for workload x."""
+    if x.kv_dtype == "fp8":
+        return "attn_partial_mfma", ("mla_attn_mfma.hip", "mla_device.h", "mla_split.h")
+    if x.n_h % 128 == 0:
+        return "attn_partial_h128", ("mla_attn_h128.hip", "mla_device.h", "mla_split.h")
+    return "attn_partial_split", ("mla_attn_mfma.hip", "mla_device.h", "mla_split.h")
+
+
+def source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 WORKLOADS = ("v3_decode_b64_l4096", "v3_paged_b128", "v3_mtp_b32_l32768", "v3_long_fp8_b4_l131072")
 
@@ -210,6 +228,7 @@ def pmc_summary(args):
     """Attention-kernel HBM traffic from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by the
     ratio the same counter shows for the plain copy kernel of known size in the same run."""
     import sqlite3
+    kname, ksrc = attn_kernel(make_workload(args.workload))
     vals = {}   # (kernel kind, counter) -> per-dispatch totals
     for path in args.pmc_summary:
         db = sqlite3.connect(path)
@@ -218,7 +237,7 @@ def pmc_summary(args):
         per = {}
         for r in db.execute("select * from counters_collection"):
             name, ctr = r[ci["kernel_name"]], r[ci["counter_name"]]
-            kind = "attn" if "attn_partial" in name else ("copy" if "neg_kernel" in name else None)
+            kind = "attn" if kname in name else ("copy" if "neg_kernel" in name else None)
             if kind is None or ctr not in ("FETCH_SIZE", "WRITE_SIZE"):
                 continue
             key = (kind, ctr, path, r[ci["dispatch_id"]])
@@ -237,7 +256,8 @@ def pmc_summary(args):
     write = mean[("attn", "WRITE_SIZE")] * 1024 / f_write
     rec = {"bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch), "write_bytes": round(write),
            "copy_factor_fetch": round(f_read, 4), "copy_factor_write": round(f_write, 4),
-           "attn_dispatches": len(vals[("attn", "FETCH_SIZE")]), "command": args.pmc_command}
+           "attn_dispatches": len(vals[("attn", "FETCH_SIZE")]), "command": args.pmc_command,
+           "kernel": kname, "source_digest": source_digest(ksrc)}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     data = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
     data[args.workload] = rec
@@ -302,16 +322,18 @@ def main():
           f"attention {attn_ms * 1e3:.1f} us, combine {comb_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     alg = algorithmic(x)
+    kname, ksrc = attn_kernel(x)
     attn_gbs = alg["attn_bytes"] / (attn_ms * 1e-3) / 1e9
     attn_tflops = alg["attn_flops"] / (attn_ms * 1e-3) / 1e12
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE)).get(args.workload)
-        if rec:
+        # Counters taken on another kernel, or on an older source of this one, do not count.
+        if rec and rec.get("kernel") == kname and rec.get("source_digest") == source_digest(ksrc):
             traffic = rec.get("bytes_per_launch")
     roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": ATTN_KERNEL[x.kv_dtype], "kernel_us": round(attn_ms * 1e3, 2),
+            "kernel": kname, "kernel_us": round(attn_ms * 1e3, 2),
             "mfma_tflops": round(attn_tflops, 1), "mfma_frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
             "algorithmic_bytes_per_launch": alg["attn_bytes"], "algorithmic_flops_per_launch": alg["attn_flops"]}
     result = {

@@ -1,0 +1,456 @@
+// Partial attention of absorbed MLA decode on gfx950, bf16 latent cache, 128 heads
+// of one query position per workgroup.
+//
+// For every piece of the split rule and every head i of the workgroup:
+//   s_j = softmax_scale * (q_nope_i . c_j + q_pe_i . k_pe_j)       (page "MLA deep compression":
+//   lse = ln sum_j exp(s_j),   u_i = sum_j exp(s_j - lse) c_j        absorbed scores, decoupled
+//                                                                   RoPE, latent accumulation u_i)
+// Every head reads the same 576-wide cached row and its first 512 values are also the
+// value row, so a workgroup that holds all 128 heads streams each cached row from HBM
+// exactly once.
+//
+// Four waves, one per SIMD, each with the whole 512-entry register file.  The two
+// contractions are split differently, because LDS read instructions, not bytes, are
+// the scarce resource (about 8 clocks of the CU's LDS pipe per wave-level read, 64-bit
+// or 128-bit alike):
+//  - scores: wave w owns heads 32w .. 32w+31, keeps their queries in registers (144)
+//    and computes S^T[token, head] = K Q^T on 32x32x16 MFMAs (36 128-bit reads of the
+//    tile per wave), then their softmax on the MFMA output layout (lane l owns head l%32
+//    and 16 tokens);
+//  - latent accumulation: wave w owns latent columns 128w .. 128w+127 of all 128 heads,
+//    U^T[col, head] += V^T P^T (4 x 4 blocks of 32 x 32, 256 accumulator registers).
+//    It reads only its quarter of the value tile (16 transposed 64-bit reads) and the
+//    probabilities of all heads (8 128-bit reads) from a small LDS exchange buffer that
+//    every wave fills with its heads' softmax output.
+// The k-order of the accumulation MFMA is chosen so that a lane's softmax output is
+// already a B operand (written to the exchange buffer as is), and the transposed reads
+// of V fetch the tokens in the same order.  Per 32-token tile t a wave runs the score
+// MFMAs of t interleaved one to one with the accumulation MFMAs of tile t-1, then the
+// softmax of t.  One barrier per tile orders the tile ring and the exchange buffer.
+//
+// LDS: a 4-deep ring of 32 x 1024-byte latent rows (tile t-1 is still read by the
+// accumulation while tile t is scored and t+1, t+2 are in flight), a 3-deep ring of
+// 32 x 128-byte RoPE-key rows (read only by the scores) and two 8 KiB probability
+// buffers (tile t-1 read while tile t is written).  The rings are filled by direct
+// buffer->LDS copies with the streaming cache policy; each wave issues 9 of a tile's
+// 36 one-KiB copies.  16-byte chunk c of latent row r is stored at c ^ sv(r),
+// sv(r) = 4 (r % 4) + (r / 4) % 4 (the two halves of r's low nibble swapped): 16
+// consecutive rows get 16 different positions (score reads: 16 rows, one chunk) and 4
+// consecutive rows 4 different 64-byte groups (transposed reads: 4 rows, four chunks
+// per 32 lanes), so neither pattern has bank conflicts.  Chunk c of RoPE row r is
+// stored at c ^ ((r / 2) % 8) (128-byte rows: 16 rows, one chunk, 16 positions).
+//
+// Softmax reference: exp2(s - m) with any m gives the same softmax once U and the sum
+// are divided by the sum, and float32 / bf16 keep their relative precision for
+// probabilities up to 2^64, so each head's reference m is fixed at the maximum of its
+// first visible tile and the accumulators are never rescaled.  If a later tile exceeds
+// m by more than 64 (log2 units), the workgroup recomputes the piece with m = the exact
+// maximum, which the first pass has seen by then.
+
+#include "mla_device.h"
+#include "mla_kernels.h"
+#include "mla_split.h"
+
+namespace mla {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kDc = 512;
+constexpr int kDr = 64;
+constexpr int kT = 32;                        // tokens per tile
+constexpr int kHeads = 128;                   // heads per workgroup
+constexpr int kWaves = 4;
+constexpr int kVRow = kDc * 2;                // 1024 bytes of latent per token
+constexpr int kVTile = kT * kVRow;            // 32 KiB
+constexpr int kKRow = kDr * 2;                // 128 bytes of RoPE key per token
+constexpr int kKTile = kT * kKRow;            // 4 KiB
+constexpr int kVRing = 4;
+constexpr int kKRing = 3;
+constexpr int kQk = (kDc + kDr) / 16;         // 36 score k-steps of 16
+constexpr int kQkV = kDc / 16;                // the first 32 read latent rows; the last 4 the RoPE part
+constexpr int kPv = 32;                       // accumulation MFMAs per tile: 2 token halves x 4 x 4 blocks
+constexpr int kCopies = 9;                    // per wave and tile: 8 latent rows + 1 RoPE block
+constexpr int kPBuf = kT * kHeads * 2;        // 8 KiB of bf16 probabilities per tile
+constexpr float kHeadroom = 64.f;             // tolerated excess over the reference maximum (log2 units)
+
+struct Smem {
+  unsigned char v[kVRing][kVTile];
+  unsigned char k[kKRing][kKTile];
+  unsigned char p[2][kPBuf];                  // [tile % 2][head block][token half][lane] x 16 bytes
+  float l[kHeads];                            // row sums, for the column-owning waves
+  int redo[kWaves];                           // per wave: a tile exceeded the reference maximum
+};
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget of one workgroup");
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  // C[32x32] += A[32x16] B[16x32]: lane l holds A[l%32][8(l/32) + j], B[8(l/32) + j][l%32]
+  // (j = 0..7) and C[8(v/4) + 4(l/32) + v%4][l%32] (v = 0..15).
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The score chain (36 MFMAs into one 32x32 block) is written in assembly so that its
+// accumulator lives in VGPRs: the latent accumulators take all 256 AGPRs, and the
+// compiler gives every MFMA of a kernel the same accumulator register file.  Hazards of
+// these instructions, which the compiler does not see:
+//  - the first MFMA of a chain starts from the inline constant 0, so no VALU write of
+//    its accumulator precedes it; the later ones read the previous result as srcC with
+//    exactly the same registers, the back-to-back accumulation case the matrix unit
+//    forwards;
+//  - each MFMA starts with s_nop 1, covering a VALU write of its A/B registers just
+//    before it (2 wait states);
+//  - scores_ready() inserts 24 wait states (more than passes + 2) before any other
+//    instruction reads or overwrites the accumulator.
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void score_mfma_first(f32x16& s, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+               : "=&v"(s)
+               : "v"(__builtin_bit_cast(u32x4v, a)), "v"(__builtin_bit_cast(u32x4v, b)));
+}
+__device__ __forceinline__ void score_mfma(f32x16& s, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+               : "+v"(s)
+               : "v"(__builtin_bit_cast(u32x4v, a)), "v"(__builtin_bit_cast(u32x4v, b)));
+}
+__device__ __forceinline__ void scores_ready(f32x16& s) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
+}
+
+// A zero the compiler cannot see through: per-lane LDS offsets derived from it are
+// recomputed where they are used (one v_xor each) instead of being hoisted out of the
+// tile loop as two dozen long-lived registers.
+__device__ __forceinline__ uint32_t opaque_zero() {
+  uint32_t z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+__device__ __forceinline__ int swz_v(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left alone
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_partial_h128(const AttnParams p) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+
+  const int w = blockIdx.x;
+  const int rg = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const int groups_per_q = p.n_h / kHeads;
+  const int q_pos = rg / groups_per_q;
+  const int head_base = (rg - q_pos * groups_per_q) * kHeads;
+  int32_t* table = (rg == 0 && wave == 0) ? p.split_table : nullptr;
+
+  // ---- fixed per-lane LDS offsets ----
+  // Score reads: token l32, logical chunk 2 ks + h, stored at (2 ks + h) ^ sv(l32).
+  const int qk_v = l32 * kVRow + 16 * (h ^ swz_v(l32));            // ^ 32 (ks % 8), + 256 (ks / 8)
+  const int qk_k = l32 * kKRow + 16 * (h ^ swz_k(l32));             // ^ 32 (ks - 32)
+  // Transposed latent reads: 16-lane block b1 = (lane/16)%2 gives columns 16 b1 .. +15 of a
+  // 32-column block, lane 4r + q of the block the 4 columns 4q.. of token row r.
+  const int tr_i = lane & 15;
+  const int tr_r = tr_i >> 2, tr_q = tr_i & 3;
+  const int tr_b1 = (lane >> 4) & 1;
+  const int tr_lc = (2 * tr_b1 + (tr_q >> 1)) ^ (4 * tr_r + h);     // rows 4h + r (+ 8 e): sv = 4r + h + 2e
+  const int tr_base = (4 * h + tr_r) * kVRow + 16 * tr_lc + 8 * (tr_q & 1) + 256 * wave;
+  const uint32_t p_base = (uint32_t)(kVRing * kVTile + kKRing * kKTile) + 16 * lane;   // + tile buffer, block
+
+  // The latent ring starts zeroed: the accumulation step that runs before a piece's
+  // first tile reads a ring slot with zero probabilities, and 0 * (stale bits) must
+  // not produce NaN.  Afterwards the ring only ever holds cache rows.
+  for (int i = threadIdx.x; i < kVRing * kVTile / 16; i += 64 * kWaves)
+    ((u32x4*)sm.v)[i] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();   // before any wave's first tile copies land in the ring
+
+  for_each_piece_wave(p.seq_lens, p.batch, p.max_tokens, p.num_splits, w, table, [&](const Piece& pc) {
+    const int L = clamp_len(p.seq_lens[pc.b], p.max_tokens);
+    const int t0 = pc.t0;
+    const int end = min(pc.t1, max(0, L - p.s_q + q_pos + 1));      // visible tokens of this piece
+    const int ntiles = end > t0 ? (end - t0 + kT - 1) / kT : 0;
+    const size_t row_base = ((size_t)pc.slot * p.s_q + q_pos) * p.n_h + head_base;
+    PageWindow pw;
+    pw.init(p.block_table + (size_t)pc.b * p.max_pages, p.max_pages, p.num_pages, t0 / p.page_size);
+    const int tiles_per_page = p.page_size / kT;
+    const uint32_t c_row = (uint32_t)p.c_stride * 2u, k_row = (uint32_t)p.k_stride * 2u;
+
+    // Copy cursor: the next tile to enqueue, its logical page, its tile index within
+    // that page and its ring slots.
+    int i_tt, i_lp, i_tip, i_vs, i_ks;
+    auto reset_cursor = [&]() {
+      i_tt = t0;
+      i_lp = t0 / p.page_size;
+      i_tip = (t0 - i_lp * p.page_size) / kT;
+      i_vs = 0;
+      i_ks = 0;
+    };
+    // Enqueue this wave's 9 copies of the cursor's tile and advance; false if its page
+    // is invalid (nothing enqueued).
+    auto issue_next = [&]() {
+      const int page = pw.get(i_lp);
+      bool ok = false;
+      if (page >= 0) {
+        const int last = min(i_tt + kT, end) - 1 - i_tt;   // rows past `last` re-read it
+        const long long slot0 = (long long)page * p.page_size + i_tip * kT;
+        // Buffer resources based at the tile's first row (a tile never crosses a page):
+        // row offsets stay far below the 2 GiB record limit.
+        const __amdgpu_buffer_rsrc_t vres = buffer_rsrc((const char*)p.c_kv + slot0 * c_row);
+        const __amdgpu_buffer_rsrc_t kres = buffer_rsrc((const char*)p.k_pe + slot0 * k_row);
+        unsigned char* vdst = sm.v[i_vs] + 8 * wave * kVRow;
+        const uint32_t lz = (uint32_t)lane + opaque_zero();
+#pragma unroll
+        for (int r8 = 0; r8 < 8; ++r8) {
+          const int r = 8 * wave + r8;
+          buffer_to_lds16(vres, 16u * (lz ^ (uint32_t)swz_v(r)), (uint32_t)min(r, last) * c_row, vdst + r8 * kVRow);
+        }
+        // RoPE block: lane l copies row 8 wave + l/8, stored chunk l%8 (recomputed here
+        // from the lane index rather than kept live across the tile loop).
+        const int krow = 8 * wave + (int)(lz >> 3);
+        const uint32_t kchunk = (lz & 7u) ^ (uint32_t)swz_k(krow);
+        const uint32_t koff = (uint32_t)min(krow, last) * k_row + 16u * kchunk;
+        buffer_to_lds16(kres, koff, 0u, sm.k[i_ks] + wave * 1024);
+        ok = true;
+      }
+      i_tt += kT;
+      if (++i_tip == tiles_per_page) {
+        i_tip = 0;
+        ++i_lp;
+      }
+      i_vs = (i_vs + 1) & (kVRing - 1);
+      i_ks = i_ks == kKRing - 1 ? 0 : i_ks + 1;
+      return ok;
+    };
+
+    // Queries of head 32 wave + l32, k-steps of 16: lane holds dims 16 ks + 8 h .. +7.
+    bf16x8 qf[kQk];
+    {
+      const size_t qrow = ((size_t)pc.b * p.s_q + q_pos) * p.n_h + head_base + 32 * wave + l32;
+      const bf16* qn = (const bf16*)p.q_nope + qrow * kDc + 8 * h;
+      const bf16* qp = (const bf16*)p.q_pe + qrow * kDr + 8 * h;
+#pragma unroll
+      for (int ks = 0; ks < kQkV; ++ks) qf[ks] = *(const bf16x8*)(qn + 16 * ks);
+#pragma unroll
+      for (int kk = 0; kk < kQk - kQkV; ++kk) qf[kQkV + kk] = *(const bf16x8*)(qp + 16 * kk);
+    }
+    f32x16 acc[16];   // U^T block (column block 4 wave + a / 4, head block a % 4)
+    float m_ref = -INFINITY;       // this lane's head's reference maximum (base 2)
+    float x_max = -INFINITY;       // largest log2 score above m_ref among this lane's tokens
+    float l_part = 0.f;
+
+    // One pass over the piece.  The accumulation of tile it-1 runs in every iteration;
+    // before the first tile it uses zero probabilities (and reads a ring slot that holds
+    // zeros or cache rows), and a tile that is not scored (invalid page, past the end)
+    // yields zero probabilities, so every iteration runs the same instruction sequence.
+    auto run_pass = [&]() {
+#pragma unroll
+      for (int a = 0; a < 16; ++a)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[a][v] = 0.f;
+      l_part = 0.f;
+      x_max = -INFINITY;
+      // Zero probabilities of "tile -1" (buffer 1), this wave's head block.
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        *(u32x4*)(sm.p[1] + (wave * 2 + half) * 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+      wait_vmcnt<0>();
+      reset_cursor();
+      // Bit k of `ready`: tile it + k has been enqueued (its page is valid).
+      uint32_t ready = 0;
+      if (ntiles > 0) ready |= issue_next() ? 1u : 0u;
+      if (ntiles > 1) ready |= issue_next() ? 2u : 0u;
+      int vs = 0, ks3 = 0;   // ring slots of tile `it`
+      for (int it = 0; it <= ntiles; ++it) {
+        if (ready & 2u)
+          wait_vmcnt<kCopies>();   // this wave's copies of tile `it` have landed, it+1's in flight
+        else
+          wait_vmcnt<0>();
+        lds_barrier();             // tile `it` and every wave's probabilities of it-1 are in LDS
+        if (it + 2 < ntiles) ready |= issue_next() ? 4u : 0u;
+        const bool cur = (ready & 1u) != 0;       // tile `it` is scored
+
+        // Per-lane LDS offsets of this iteration: ring slot + fixed lane part; the XOR
+        // swizzles only touch bits 4..7, below the slot bits.
+        const unsigned char* lds = (const unsigned char*)&sm;
+        const uint32_t z = opaque_zero();
+        const uint32_t bq = (uint32_t)(vs * kVTile) + qk_v + z;
+        const uint32_t bk = (uint32_t)(kVRing * kVTile + ks3 * kKTile) + qk_k + z;
+        const uint32_t bt = (uint32_t)(((vs + kVRing - 1) & (kVRing - 1)) * kVTile) + tr_base + z;
+        const uint32_t bp = p_base + (uint32_t)(((it + 1) & 1) * kPBuf) + z;
+        auto kfrag = [&](int ks) -> bf16x8 {
+          if (ks < kQkV) return *(const bf16x8*)(lds + ((bq ^ (32u * (ks & 7))) + 256 * (ks >> 3)));
+          return *(const bf16x8*)(lds + (bk ^ (32u * (ks - kQkV))));
+        };
+        // V^T fragment of this wave's column block cl (32 columns) and token half th of
+        // tile it-1.
+        auto vfrag = [&](int cl, int th) -> bf16x8 {
+          const uint32_t o = 16384 * th;
+          const bf16x4 lo = lds_read_tr16(lds + ((bt ^ (64u * cl)) + o));
+          const bf16x4 hi = lds_read_tr16(lds + ((bt ^ (64u * cl ^ 32u)) + o + 8192));
+          return concat4(lo, hi);
+        };
+        // P^T fragment of head block hb and token half th of tile it-1.
+        auto pfrag = [&](int hb, int th) -> bf16x8 { return *(const bf16x8*)(lds + bp + (hb * 2 + th) * 1024); };
+
+        // Accumulation step a of tile it-1: token half a / 16, column block (a / 4) % 4,
+        // head block a % 4.  Phase 1: the 36 score MFMAs of tile `it` (one dependent
+        // chain) with steps 0..15 between every other pair of them; phase 2: the softmax
+        // of tile `it` interleaved with steps 16..31.  LDS operands are read ahead: with
+        // one wave per SIMD the reads' latency has to hide behind this wave's own MFMAs.
+        f32x16 s;
+        bf16x8 kq[3], va[4], pb[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) kq[j] = kfrag(j);
+        va[0] = vfrag(0, 0);
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) pb[0][hb] = pfrag(hb, 0);
+#pragma unroll
+        for (int ks = 0; ks < kQk; ++ks) {
+          __builtin_amdgcn_sched_barrier(0);   // keep the source order: reads ahead of use
+          if (ks + 2 < kQk) kq[(ks + 2) % 3] = kfrag(ks + 2);
+          // Step a runs at ks = 2a + 3.  va[cl] holds token half 0 of column block cl
+          // until its last use at ks = 8 cl + 9, then token half 1 (loaded 3 steps later).
+          if (ks == 2) va[1] = vfrag(1, 0);
+          if (ks == 10) va[2] = vfrag(2, 0);
+          if (ks == 18) va[3] = vfrag(3, 0);
+          if (ks == 12) va[0] = vfrag(0, 1);
+          if (ks == 20) va[1] = vfrag(1, 1);
+          if (ks == 28) va[2] = vfrag(2, 1);
+          if (ks >= 30 && ks < 34) pb[1][ks - 30] = pfrag(ks - 30, 1);
+          if (ks == 35) va[3] = vfrag(3, 1);
+          if (ks == 0)
+            score_mfma_first(s, kq[ks % 3], qf[ks]);
+          else
+            score_mfma(s, kq[ks % 3], qf[ks]);
+          if (ks >= 3 && ks % 2 == 1 && ks < 35) {
+            const int a = (ks - 3) / 2;
+            acc[a] = mfma32(va[a / 4], pb[0][a % 4], acc[a]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Softmax numerators of tile `it`, base 2.  Lane owns head l32 and tokens
+        // 8(v/4) + 4h + v%4; tokens at or past `rem` (all, if the tile is not scored)
+        // are masked.
+        scores_ready(s);
+        const int tt = t0 + it * kT;
+        const int rem = cur ? end - tt : 0;
+        if (__builtin_amdgcn_readfirstlane(m_ref == -INFINITY ? 1 : 0) && cur) {
+          // First scored tile: its maximum becomes the reference of this head (the same
+          // tile for every head, since visibility depends only on the token).
+          float mx = -INFINITY;
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (8 * (v >> 2) + 4 * h + (v & 3) < rem) mx = fmaxf(mx, s[v] * p.scale_log2);
+          m_ref = max_xor32(mx);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
+        const int rem_h = rem - 4 * h;
+        float x[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          x[v] = 8 * (v >> 2) + (v & 3) < rem_h ? __builtin_fmaf(s[v], p.scale_log2, nm) : -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) x_max = fmaxf(x_max, fmaxf(x[v], x[v + 1]));
+        float psum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          x[v] = exp2_fast(x[v]);
+          psum += x[v];
+        }
+        l_part += psum;
+        // Token half `half` of this lane's probabilities is the B operand (head block
+        // `wave`, token half `half`) of the accumulation: store it as is.
+        unsigned char* pout = sm.p[it & 1] + wave * 2 * 1024 + 16 * lane;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          bf16x8 pf;
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            const bf16x2 t = pack_bf16(x[8 * half + j], x[8 * half + j + 1]);
+            pf[j] = t[0];
+            pf[j + 1] = t[1];
+          }
+          *(bf16x8*)(pout + half * 1024) = pf;
+        }
+#pragma unroll
+        for (int a = 16; a < kPv; ++a) acc[a - 16] = mfma32(va[(a - 16) / 4], pb[1][a % 4], acc[a - 16]);
+        // Interleave: one accumulation MFMA, then a share of the softmax.
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        ready >>= 1;
+        vs = (vs + 1) & (kVRing - 1);
+        ks3 = ks3 == kKRing - 1 ? 0 : ks3 + 1;
+      }
+    };
+
+    run_pass();
+    // A tile above the reference by more than the headroom: every wave learns it and
+    // the piece is recomputed with the exact maximum (over both lane halves of each
+    // head) as the reference.
+    const bool excess = __any(x_max > kHeadroom);   // vote of all 64 lanes
+    if (lane == 0) sm.redo[wave] = excess ? 1 : 0;
+    __syncthreads();
+    const bool redo = (sm.redo[0] | sm.redo[1] | sm.redo[2] | sm.redo[3]) != 0;
+    __syncthreads();
+    if (redo) {
+      m_ref += max_xor32(x_max);
+      run_pass();
+    }
+
+    // Epilogue: u = U / l.  Row sums go through LDS to the column-owning waves.
+    const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
+    if (h == 0) {
+      sm.l[32 * wave + l32] = l_tot;
+      p.part_lse[row_base + 32 * wave + l32] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const float lt = sm.l[32 * hb + l32];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      float* up = p.part_u + (row_base + 32 * hb + l32) * kDc + 128 * wave + 4 * h;
+#pragma unroll
+      for (int cl = 0; cl < 4; ++cl)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          __builtin_amdgcn_sched_barrier(0);
+          f32x4 o;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) o[k] = acc[4 * cl + hb][4 * g4 + k] * inv;
+          *(f32x4*)(up + 32 * cl + 8 * g4) = o;
+        }
+    }
+    // The next piece's prologue refills ring slots 0 and 1 and the row sums, which other
+    // waves may still be reading for this piece.
+    __syncthreads();
+  });
+}
+
+}  // namespace
+
+hipError_t launch_attn_h128(const AttnParams& p, hipStream_t stream) {
+  if (p.n_h % kHeads != 0 || p.d_c != kDc || p.d_r != kDr) return hipErrorInvalidValue;
+  dim3 grid(p.num_splits, p.s_q * (p.n_h / kHeads));
+  hipLaunchKernelGGL(attn_partial_h128, grid, dim3(64 * kWaves), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

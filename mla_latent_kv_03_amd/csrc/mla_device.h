@@ -48,6 +48,24 @@ __device__ __forceinline__ void global_to_lds16(const void* gsrc, void* lds_wave
   __builtin_amdgcn_global_load_lds(gsrc, (MLA_LDS void*)(lds_wave_base), 16, 0, kCachePolicyNT);
 }
 
+// The same copy through a buffer resource: lane l reads base + soffset + voffset_l.
+// `base` and `soffset` must be wave-uniform.  The compiler tracks these (MUBUF) copies
+// as ordinary vector-memory operations, whereas a global_load_lds in a loop makes it
+// wait for every outstanding LDS read (lgkmcnt(0)) before the next LDS use, which
+// defeats software prefetching of LDS operands.  The 2 GiB record limit is only a
+// bound on voffset + soffset.
+constexpr int kBufferWord3 = 0x00020000;   // gfx9-family raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, kBufferWord3);
+}
+
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t soffset,
+                                                void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(lds_wave_base), 16, voffset, soffset, 0,
+                                           kCachePolicyNT);
+}
+
 __device__ __forceinline__ bf16x8 concat4(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }

@@ -57,6 +57,7 @@ struct AppendParams {
 // Heads of one query position handled by one workgroup of the bf16 kernel.
 int attn_heads_per_group(int n_h);
 hipError_t launch_attn_mfma(const AttnParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_attn_h128(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_fp8_v0(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
 hipError_t launch_combine_bf16(const CombineParams& p, hipStream_t stream);

@@ -123,3 +123,27 @@ def test_v3_long_fp8_b4_l131072():
     assert case.binding.mla_decode_num_splits(case.params) == 256 or torch.cuda.get_device_properties(0).multi_processor_count != 256
     out, lse, _ = case.run()
     compare_sampled(case, out, lse, [0, 3], BF16_TOL, lse_tol=5e-3, what="v3 long fp8")
+
+
+# ---------------------------------------------------------------- scores far above the first tile's
+
+@pytest.mark.parametrize("G", [0, 3])
+def test_late_dominant_token(G):
+    """A token deep in the sequence whose scores exceed everything before it by far
+    more than 2^64 (its latent is a large multiple of the heads' mean query direction):
+    softmax is dominated by it, and the kernels must still match the float64 oracle."""
+    _print_case("late_dominant_token", G=G)
+    import torch
+    x = workloads.make_decode([2049, 700], n_h=128, page_size=64, seed=77)
+    qdir = torch.sign(x.q_nope[0, 0].float().mean(dim=0))          # [d_c]
+    for b, t in ((0, 1500), (1, 650)):
+        slot = int(x.block_table[b, t // x.page_size]) * x.page_size + t % x.page_size
+        x.pool[slot, :x.d_c] = (30.0 * qdir).to(x.pool.dtype)
+    case = DeviceCase(x, num_splits=G)
+    out, lse, _ = case.run()
+    # The outputs here reach |o| ~ 100 (u is dominated by a latent of magnitude 30), and the
+    # bf16 output alone rounds by up to |o| 2^-9: the absolute bound scales with the output
+    # (a few bf16 steps of the largest value); the relative bound is the usual one.
+    o_ref, _ = case.oracle([0, 1])
+    tol = dict(rel_l2=BF16_TOL["rel_l2"], max_abs=max(BF16_TOL["max_abs"], 2.0 ** -7 * float(np.abs(o_ref).max())))
+    compare_sampled(case, out, lse, [0, 1], tol, lse_tol=5e-3, what="late dominant token")
