@@ -24,9 +24,11 @@
 //    every wave fills with its heads' softmax output.
 // The k-order of the accumulation MFMA is chosen so that a lane's softmax output is
 // already a B operand (written to the exchange buffer as is), and the transposed reads
-// of V fetch the tokens in the same order.  Per 32-token tile t a wave runs the score
-// MFMAs of t interleaved one to one with the accumulation MFMAs of tile t-1, then the
-// softmax of t.  One barrier per tile orders the tile ring and the exchange buffer.
+// of V fetch the tokens in the same order.  Per 32-token tile t a wave runs the 36
+// score MFMAs of t (one dependent chain) with half of the accumulation MFMAs of tile
+// t-1 between them, then the softmax of t interleaved with the other half, and spreads
+// its 9 tile copies of t+2 over the score steps.  One barrier per tile orders the tile
+// ring and the exchange buffer.
 //
 // LDS: a 4-deep ring of 32 x 1024-byte latent rows (tile t-1 is still read by the
 // accumulation while tile t is scored and t+1, t+2 are in flight), a 3-deep ring of
@@ -125,6 +127,14 @@ __device__ __forceinline__ uint32_t opaque_zero() {
   return z;
 }
 
+// The lane index, computed where it is used (the compiler cannot tie it to a value it
+// already holds, which would keep that value live across the tile loop).
+__device__ __forceinline__ uint32_t lane_id_opaque() {
+  uint32_t l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ int swz_v(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
 
@@ -196,33 +206,27 @@ void attn_partial_h128(const AttnParams p) {
       i_vs = 0;
       i_ks = 0;
     };
-    // Enqueue this wave's 9 copies of the cursor's tile and advance; false if its page
-    // is invalid (nothing enqueued).
-    auto issue_next = [&]() {
-      const int page = pw.get(i_lp);
-      bool ok = false;
-      if (page >= 0) {
-        const int last = min(i_tt + kT, end) - 1 - i_tt;   // rows past `last` re-read it
-        const long long slot0 = (long long)page * p.page_size + i_tip * kT;
-        // Buffer resources based at the tile's first row (a tile never crosses a page):
-        // row offsets stay far below the 2 GiB record limit.
-        const __amdgpu_buffer_rsrc_t vres = buffer_rsrc((const char*)p.c_kv + slot0 * c_row);
-        const __amdgpu_buffer_rsrc_t kres = buffer_rsrc((const char*)p.k_pe + slot0 * k_row);
-        unsigned char* vdst = sm.v[i_vs] + 8 * wave * kVRow;
-        const uint32_t lz = (uint32_t)lane + opaque_zero();
-#pragma unroll
-        for (int r8 = 0; r8 < 8; ++r8) {
-          const int r = 8 * wave + r8;
-          buffer_to_lds16(vres, 16u * (lz ^ (uint32_t)swz_v(r)), (uint32_t)min(r, last) * c_row, vdst + r8 * kVRow);
-        }
-        // RoPE block: lane l copies row 8 wave + l/8, stored chunk l%8 (recomputed here
-        // from the lane index rather than kept live across the tile loop).
-        const int krow = 8 * wave + (int)(lz >> 3);
-        const uint32_t kchunk = (lz & 7u) ^ (uint32_t)swz_k(krow);
-        const uint32_t koff = (uint32_t)min(krow, last) * k_row + 16u * kchunk;
-        buffer_to_lds16(kres, koff, 0u, sm.k[i_ks] + wave * 1024);
-        ok = true;
-      }
+    // Copies of one tile by this wave: buffer resources based at the tile's first latent
+    // and RoPE rows (a tile never crosses a page, so row offsets stay far below the
+    // 2 GiB record limit), its last visible row and its ring slots.  A tile with an
+    // invalid page, or past the piece, gets zero-length resources: its copies read
+    // nothing and fill their ring slots with zeros.
+    struct TileCopy {
+      __amdgpu_buffer_rsrc_t vres, kres;
+      int last, vs, ks;
+    };
+    // Describe the cursor's tile and advance the cursor (scalar work only); `ok` tells
+    // whether the tile has a valid page.
+    auto prepare_next = [&](bool exists, bool& ok) {
+      TileCopy tc;
+      const int page = exists ? pw.get(i_lp) : -1;
+      ok = page >= 0;
+      const long long slot0 = ok ? (long long)page * p.page_size + i_tip * kT : 0;
+      tc.vres = buffer_rsrc((const char*)p.c_kv + slot0 * c_row, ok ? 0x7fffffff : 0);
+      tc.kres = buffer_rsrc((const char*)p.k_pe + slot0 * k_row, ok ? 0x7fffffff : 0);
+      tc.last = min(i_tt + kT, end) - 1 - i_tt;   // rows past `last` re-read it
+      tc.vs = i_vs;
+      tc.ks = i_ks;
       i_tt += kT;
       if (++i_tip == tiles_per_page) {
         i_tip = 0;
@@ -230,7 +234,23 @@ void attn_partial_h128(const AttnParams p) {
       }
       i_vs = (i_vs + 1) & (kVRing - 1);
       i_ks = i_ks == kKRing - 1 ? 0 : i_ks + 1;
-      return ok;
+      return tc;
+    };
+    // Copy j of this wave's 9 for tile tc: latent row 8 wave + j (j < 8; lane l: stored
+    // chunk l) or the RoPE block (j = 8; lane l: row 8 wave + l/8, stored chunk l%8).
+    // Per-lane offsets are recomputed from the lane index rather than kept live.
+    auto copy_row = [&](const TileCopy& tc, int j) {
+      const uint32_t lz = (uint32_t)lane + opaque_zero();
+      if (j < 8) {
+        const int r = 8 * wave + j;
+        buffer_to_lds16(tc.vres, 16u * (lz ^ (uint32_t)swz_v(r)), (uint32_t)min(r, tc.last) * c_row,
+                        sm.v[tc.vs] + r * kVRow);
+      } else {
+        const int krow = 8 * wave + (int)(lz >> 3);
+        const uint32_t kchunk = (lz & 7u) ^ (uint32_t)swz_k(krow);
+        const uint32_t koff = (uint32_t)min(krow, tc.last) * k_row + 16u * kchunk;
+        buffer_to_lds16(tc.kres, koff, 0u, sm.k[tc.ks] + wave * 1024);
+      }
     };
 
     // Queries of head 32 wave + l32, k-steps of 16: lane holds dims 16 ks + 8 h .. +7.
@@ -266,19 +286,28 @@ void attn_partial_h128(const AttnParams p) {
         *(u32x4*)(sm.p[1] + (wave * 2 + half) * 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
       wait_vmcnt<0>();
       reset_cursor();
-      // Bit k of `ready`: tile it + k has been enqueued (its page is valid).
+      // Bit k of `ready`: tile it + k has a valid page.  Every iteration enqueues the 9
+      // copies of tile it + 2 (no-ops past the piece), so exactly one tile's copies are
+      // in flight besides tile it's at the top of an iteration.
       uint32_t ready = 0;
-      if (ntiles > 0) ready |= issue_next() ? 1u : 0u;
-      if (ntiles > 1) ready |= issue_next() ? 2u : 0u;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bool ok;
+        const TileCopy tc = prepare_next(t < ntiles, ok);
+        ready |= ok ? (1u << t) : 0u;
+#pragma unroll
+        for (int j = 0; j < kCopies; ++j) copy_row(tc, j);
+      }
       int vs = 0, ks3 = 0;   // ring slots of tile `it`
       for (int it = 0; it <= ntiles; ++it) {
-        if (ready & 2u)
-          wait_vmcnt<kCopies>();   // this wave's copies of tile `it` have landed, it+1's in flight
-        else
-          wait_vmcnt<0>();
+        wait_vmcnt<kCopies>();     // this wave's copies of tile `it` have landed, it+1's in flight
         lds_barrier();             // tile `it` and every wave's probabilities of it-1 are in LDS
-        if (it + 2 < ntiles) ready |= issue_next() ? 4u : 0u;
         const bool cur = (ready & 1u) != 0;       // tile `it` is scored
+        bool next_ok;
+        // Tile it+2 goes to ring slots last read in iteration it-1, which every wave
+        // has finished (barrier above).
+        const TileCopy tn = prepare_next(it + 2 < ntiles, next_ok);
+        ready |= next_ok ? 4u : 0u;
 
         // Per-lane LDS offsets of this iteration: ring slot + fixed lane part; the XOR
         // swizzles only touch bits 4..7, below the slot bits.
@@ -329,6 +358,7 @@ void attn_partial_h128(const AttnParams p) {
           if (ks == 28) va[2] = vfrag(2, 1);
           if (ks >= 30 && ks < 34) pb[1][ks - 30] = pfrag(ks - 30, 1);
           if (ks == 35) va[3] = vfrag(3, 1);
+          if (ks % 4 == 1) copy_row(tn, ks / 4);                                    // ks = 1, 5, .., 33
           if (ks == 0)
             score_mfma_first(s, kq[ks % 3], qf[ks]);
           else
@@ -346,22 +376,26 @@ void attn_partial_h128(const AttnParams p) {
         scores_ready(s);
         const int tt = t0 + it * kT;
         const int rem = cur ? end - tt : 0;
+        if (rem < kT) {
+          // Last tile of the piece, or not scored: mask tokens at or past `rem`.
+          const int rem_h = rem - 4 * (int)(lane_id_opaque() >> 5);   // recomputed, not kept live
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (8 * (v >> 2) + (v & 3) >= rem_h) s[v] = -INFINITY;
+        }
         if (__builtin_amdgcn_readfirstlane(m_ref == -INFINITY ? 1 : 0) && cur) {
           // First scored tile: its maximum becomes the reference of this head (the same
           // tile for every head, since visibility depends only on the token).
-          float mx = -INFINITY;
+          float mx = s[0];
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (8 * (v >> 2) + 4 * h + (v & 3) < rem) mx = fmaxf(mx, s[v] * p.scale_log2);
-          m_ref = max_xor32(mx);
+          for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+          m_ref = max_xor32(mx) * p.scale_log2;
         }
         __builtin_amdgcn_sched_barrier(0);
         const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
-        const int rem_h = rem - 4 * h;
         float x[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          x[v] = 8 * (v >> 2) + (v & 3) < rem_h ? __builtin_fmaf(s[v], p.scale_log2, nm) : -INFINITY;
+        for (int v = 0; v < 16; ++v) x[v] = __builtin_fmaf(s[v], p.scale_log2, nm);
 #pragma unroll
         for (int v = 0; v < 16; v += 2) x_max = fmaxf(x_max, fmaxf(x[v], x[v + 1]));
         float psum = 0.f;
@@ -391,7 +425,7 @@ void attn_partial_h128(const AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // VALU
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
         }
         __builtin_amdgcn_sched_barrier(0);
 

@@ -52,12 +52,13 @@ __device__ __forceinline__ void global_to_lds16(const void* gsrc, void* lds_wave
 // `base` and `soffset` must be wave-uniform.  The compiler tracks these (MUBUF) copies
 // as ordinary vector-memory operations, whereas a global_load_lds in a loop makes it
 // wait for every outstanding LDS read (lgkmcnt(0)) before the next LDS use, which
-// defeats software prefetching of LDS operands.  The 2 GiB record limit is only a
-// bound on voffset + soffset.
+// defeats software prefetching of LDS operands.  `num_records` bounds voffset
+// (bytes); a load past it reads nothing from memory and returns zeros, so a resource
+// with num_records = 0 turns a copy into a no-op of the same instruction count.
 constexpr int kBufferWord3 = 0x00020000;   // gfx9-family raw buffer, 32-bit data format
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, kBufferWord3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int num_records = 0x7fffffff) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, num_records, kBufferWord3);
 }
 
 __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t soffset,
