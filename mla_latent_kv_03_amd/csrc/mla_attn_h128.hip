@@ -74,6 +74,10 @@ constexpr int kQkV = kDc / 16;                // the first 32 read latent rows; 
 constexpr int kPv = 32;                       // accumulation MFMAs per tile: 2 token halves x 4 x 4 blocks
 constexpr int kCopies = 9;                    // per wave and tile: 8 latent rows + 1 RoPE block
 constexpr int kPBuf = kT * kHeads * 2;        // 8 KiB of bf16 probabilities per tile
+#ifndef MLA_H128_KPF
+#define MLA_H128_KPF 2
+#endif
+constexpr int kKPf = MLA_H128_KPF;            // score operands are read this many k-steps ahead
 constexpr float kHeadroom = 64.f;             // tolerated excess over the reference maximum (log2 units)
 
 struct Smem {
@@ -127,14 +131,6 @@ __device__ __forceinline__ uint32_t opaque_zero() {
   return z;
 }
 
-// The lane index, computed where it is used (the compiler cannot tie it to a value it
-// already holds, which would keep that value live across the tile loop).
-__device__ __forceinline__ uint32_t lane_id_opaque() {
-  uint32_t l;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-  return l;
-}
-
 __device__ __forceinline__ int swz_v(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
 
@@ -158,41 +154,72 @@ void attn_partial_h128(const AttnParams p) {
   const int rg = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l32 = lane & 31;
-  const int h = lane >> 5;
   const int groups_per_q = p.n_h / kHeads;
   const int q_pos = rg / groups_per_q;
   const int head_base = (rg - q_pos * groups_per_q) * kHeads;
   int32_t* table = (rg == 0 && wave == 0) ? p.split_table : nullptr;
 
-  // ---- fixed per-lane LDS offsets ----
-  // Score reads: token l32, logical chunk 2 ks + h, stored at (2 ks + h) ^ sv(l32).
-  const int qk_v = l32 * kVRow + 16 * (h ^ swz_v(l32));            // ^ 32 (ks % 8), + 256 (ks / 8)
-  const int qk_k = l32 * kKRow + 16 * (h ^ swz_k(l32));             // ^ 32 (ks - 32)
-  // Transposed latent reads: 16-lane block b1 = (lane/16)%2 gives columns 16 b1 .. +15 of a
-  // 32-column block, lane 4r + q of the block the 4 columns 4q.. of token row r.
-  const int tr_i = lane & 15;
-  const int tr_r = tr_i >> 2, tr_q = tr_i & 3;
-  const int tr_b1 = (lane >> 4) & 1;
-  const int tr_lc = (2 * tr_b1 + (tr_q >> 1)) ^ (4 * tr_r + h);     // rows 4h + r (+ 8 e): sv = 4r + h + 2e
-  const int tr_base = (4 * h + tr_r) * kVRow + 16 * tr_lc + 8 * (tr_q & 1) + 256 * wave;
-  const uint32_t p_base = (uint32_t)(kVRing * kVTile + kKRing * kKTile) + 16 * lane;   // + tile buffer, block
+  // Per-lane LDS offsets (all recomputed from the lane index where they are used, so
+  // that none of them stays live across the tile loop):
+  //  - score reads: token l32, logical chunk 2 ks + h, stored at (2 ks + h) ^ sv(l32);
+  //  - transposed latent reads: 16-lane block b1 = (lane/16)%2 gives columns 16 b1 .. +15
+  //    of a 32-column block, lane 4r + q of the block the 4 columns 4q.. of token row r
+  //    (rows 4h + r (+ 8 e) have sv = 4r + h + 2e);
+  //  - probability buffer: 16 bytes per lane.
+  struct LaneOffsets {
+    uint32_t qk_v, qk_k, tr, pb;
+  };
+  auto lane_offsets = [&]() {
+    const uint32_t ln = lane_id_opaque();
+    const int l = (int)ln, lr = l & 31, hh = l >> 5;
+    const int tr_i = l & 15, tr_r = tr_i >> 2, tr_q = tr_i & 3, tr_b1 = (l >> 4) & 1;
+    const int tr_lc = (2 * tr_b1 + (tr_q >> 1)) ^ (4 * tr_r + hh);
+    LaneOffsets o;
+    o.qk_v = (uint32_t)(lr * kVRow + 16 * (hh ^ swz_v(lr)));                   // ^ 32 (ks % 8), + 256 (ks / 8)
+    o.qk_k = (uint32_t)(kVRing * kVTile + lr * kKRow + 16 * (hh ^ swz_k(lr)));  // ^ 32 (ks - 32)
+    o.tr = (uint32_t)((4 * hh + tr_r) * kVRow + 16 * tr_lc + 8 * (tr_q & 1) + 256 * wave);
+    o.pb = (uint32_t)(kVRing * kVTile + kKRing * kKTile) + 16 * ln;
+    return o;
+  };
 
-  // The latent ring starts zeroed: the accumulation step that runs before a piece's
-  // first tile reads a ring slot with zero probabilities, and 0 * (stale bits) must
-  // not produce NaN.  Afterwards the ring only ever holds cache rows.
-  for (int i = threadIdx.x; i < kVRing * kVTile / 16; i += 64 * kWaves)
-    ((u32x4*)sm.v)[i] = u32x4{0u, 0u, 0u, 0u};
+  const int len0 = first_lens(p.seq_lens, p.batch, p.max_tokens);   // in flight during the zeroing
+  // Ring slot 3 starts zeroed: the accumulation step that runs before a pass's first
+  // tile reads it with zero probabilities, and 0 * (stale bits) must not produce NaN.
+  // Afterwards the ring only ever holds cache rows or zeros.
+  for (int i = threadIdx.x; i < kVTile / 16; i += 64 * kWaves)
+    ((u32x4*)sm.v[kVRing - 1])[i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();   // before any wave's first tile copies land in the ring
 
-  for_each_piece_wave(p.seq_lens, p.batch, p.max_tokens, p.num_splits, w, table, [&](const Piece& pc) {
-    const int L = clamp_len(p.seq_lens[pc.b], p.max_tokens);
+  // The block-table row of the sequence this share starts in when all lengths are equal
+  // is requested now, together with the lengths, instead of after the split walk (cold
+  // loads take microseconds); a piece of another sequence loads its own row.
+  const int b_guess = min(p.batch - 1, (int)(((long long)w * p.batch) / p.num_splits));
+  PageWindow pw;
+  pw.init(p.block_table + (size_t)b_guess * p.max_pages, p.max_pages, p.num_pages, 0);
+  int pw_b = b_guess;
+
+  for_each_piece_wave(p.seq_lens, p.batch, p.max_tokens, p.num_splits, w, table, len0, [&](const Piece& pc) {
+    const int L = pc.len;
     const int t0 = pc.t0;
     const int end = min(pc.t1, max(0, L - p.s_q + q_pos + 1));      // visible tokens of this piece
     const int ntiles = end > t0 ? (end - t0 + kT - 1) / kT : 0;
     const size_t row_base = ((size_t)pc.slot * p.s_q + q_pos) * p.n_h + head_base;
-    PageWindow pw;
-    pw.init(p.block_table + (size_t)pc.b * p.max_pages, p.max_pages, p.num_pages, t0 / p.page_size);
+    if (pc.b != pw_b) {
+      pw.init(p.block_table + (size_t)pc.b * p.max_pages, p.max_pages, p.num_pages, t0 / p.page_size);
+      pw_b = pc.b;
+    }
+    // Queries of head 32 wave + l32, k-steps of 16: lane holds dims 16 ks + 8 h .. +7.
+    bf16x8 qf[kQk];
+    auto load_queries = [&]() {
+      const int ql = (int)lane_id_opaque(), l32 = ql & 31, h = ql >> 5;
+      const size_t qrow = ((size_t)pc.b * p.s_q + q_pos) * p.n_h + head_base + 32 * wave + l32;
+      const bf16* qn = (const bf16*)p.q_nope + qrow * kDc + 8 * h;
+      const bf16* qp = (const bf16*)p.q_pe + qrow * kDr + 8 * h;
+#pragma unroll
+      for (int ks = 0; ks < kQkV; ++ks) qf[ks] = *(const bf16x8*)(qn + 16 * ks);
+#pragma unroll
+      for (int kk = 0; kk < kQk - kQkV; ++kk) qf[kQkV + kk] = *(const bf16x8*)(qp + 16 * kk);
+    };
     const int tiles_per_page = p.page_size / kT;
     const uint32_t c_row = (uint32_t)p.c_stride * 2u, k_row = (uint32_t)p.k_stride * 2u;
 
@@ -200,6 +227,7 @@ void attn_partial_h128(const AttnParams p) {
     // that page and its ring slots.
     int i_tt, i_lp, i_tip, i_vs, i_ks;
     auto reset_cursor = [&]() {
+      pw.rewind(t0 / p.page_size);
       i_tt = t0;
       i_lp = t0 / p.page_size;
       i_tip = (t0 - i_lp * p.page_size) / kT;
@@ -240,7 +268,7 @@ void attn_partial_h128(const AttnParams p) {
     // chunk l) or the RoPE block (j = 8; lane l: row 8 wave + l/8, stored chunk l%8).
     // Per-lane offsets are recomputed from the lane index rather than kept live.
     auto copy_row = [&](const TileCopy& tc, int j) {
-      const uint32_t lz = (uint32_t)lane + opaque_zero();
+      const uint32_t lz = lane_id_opaque();
       if (j < 8) {
         const int r = 8 * wave + j;
         buffer_to_lds16(tc.vres, 16u * (lz ^ (uint32_t)swz_v(r)), (uint32_t)min(r, tc.last) * c_row,
@@ -253,17 +281,6 @@ void attn_partial_h128(const AttnParams p) {
       }
     };
 
-    // Queries of head 32 wave + l32, k-steps of 16: lane holds dims 16 ks + 8 h .. +7.
-    bf16x8 qf[kQk];
-    {
-      const size_t qrow = ((size_t)pc.b * p.s_q + q_pos) * p.n_h + head_base + 32 * wave + l32;
-      const bf16* qn = (const bf16*)p.q_nope + qrow * kDc + 8 * h;
-      const bf16* qp = (const bf16*)p.q_pe + qrow * kDr + 8 * h;
-#pragma unroll
-      for (int ks = 0; ks < kQkV; ++ks) qf[ks] = *(const bf16x8*)(qn + 16 * ks);
-#pragma unroll
-      for (int kk = 0; kk < kQk - kQkV; ++kk) qf[kQkV + kk] = *(const bf16x8*)(qp + 16 * kk);
-    }
     f32x16 acc[16];   // U^T block (column block 4 wave + a / 4, head block a % 4)
     float m_ref = -INFINITY;       // this lane's head's reference maximum (base 2)
     float x_max = -INFINITY;       // largest log2 score above m_ref among this lane's tokens
@@ -273,7 +290,7 @@ void attn_partial_h128(const AttnParams p) {
     // before the first tile it uses zero probabilities (and reads a ring slot that holds
     // zeros or cache rows), and a tile that is not scored (invalid page, past the end)
     // yields zero probabilities, so every iteration runs the same instruction sequence.
-    auto run_pass = [&]() {
+    auto run_pass = [&](bool first_pass) {
 #pragma unroll
       for (int a = 0; a < 16; ++a)
 #pragma unroll
@@ -283,12 +300,17 @@ void attn_partial_h128(const AttnParams p) {
       // Zero probabilities of "tile -1" (buffer 1), this wave's head block.
 #pragma unroll
       for (int half = 0; half < 2; ++half)
-        *(u32x4*)(sm.p[1] + (wave * 2 + half) * 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
-      wait_vmcnt<0>();
+        *(u32x4*)(sm.p[1] + (wave * 2 + half) * 1024 + 16 * lane_id_opaque()) = u32x4{0u, 0u, 0u, 0u};
+      // No drain of older loads here: a wave's copies land in issue order and each wave
+      // writes only its own ring rows, so an earlier pass's copies cannot overwrite
+      // this pass's; the query loads are covered by the first iteration's wait.
       reset_cursor();
       // Bit k of `ready`: tile it + k has a valid page.  Every iteration enqueues the 9
       // copies of tile it + 2 (no-ops past the piece), so exactly one tile's copies are
       // in flight besides tile it's at the top of an iteration.
+      // The queries (first pass) are requested between tiles 0 and 1: the first
+      // iteration's wait then covers exactly tile 0 and the queries, and the copies do
+      // not queue behind 36 query loads.
       uint32_t ready = 0;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -297,6 +319,7 @@ void attn_partial_h128(const AttnParams p) {
         ready |= ok ? (1u << t) : 0u;
 #pragma unroll
         for (int j = 0; j < kCopies; ++j) copy_row(tc, j);
+        if (t == 0 && first_pass) load_queries();
       }
       int vs = 0, ks3 = 0;   // ring slots of tile `it`
       for (int it = 0; it <= ntiles; ++it) {
@@ -312,11 +335,11 @@ void attn_partial_h128(const AttnParams p) {
         // Per-lane LDS offsets of this iteration: ring slot + fixed lane part; the XOR
         // swizzles only touch bits 4..7, below the slot bits.
         const unsigned char* lds = (const unsigned char*)&sm;
-        const uint32_t z = opaque_zero();
-        const uint32_t bq = (uint32_t)(vs * kVTile) + qk_v + z;
-        const uint32_t bk = (uint32_t)(kVRing * kVTile + ks3 * kKTile) + qk_k + z;
-        const uint32_t bt = (uint32_t)(((vs + kVRing - 1) & (kVRing - 1)) * kVTile) + tr_base + z;
-        const uint32_t bp = p_base + (uint32_t)(((it + 1) & 1) * kPBuf) + z;
+        const LaneOffsets lo = lane_offsets();
+        const uint32_t bq = (uint32_t)(vs * kVTile) + lo.qk_v;
+        const uint32_t bk = (uint32_t)(ks3 * kKTile) + lo.qk_k;
+        const uint32_t bt = (uint32_t)(((vs + kVRing - 1) & (kVRing - 1)) * kVTile) + lo.tr;
+        const uint32_t bp = (uint32_t)(((it + 1) & 1) * kPBuf) + lo.pb;
         auto kfrag = [&](int ks) -> bf16x8 {
           if (ks < kQkV) return *(const bf16x8*)(lds + ((bq ^ (32u * (ks & 7))) + 256 * (ks >> 3)));
           return *(const bf16x8*)(lds + (bk ^ (32u * (ks - kQkV))));
@@ -338,16 +361,16 @@ void attn_partial_h128(const AttnParams p) {
         // of tile `it` interleaved with steps 16..31.  LDS operands are read ahead: with
         // one wave per SIMD the reads' latency has to hide behind this wave's own MFMAs.
         f32x16 s;
-        bf16x8 kq[3], va[4], pb[2][4];
+        bf16x8 kq[kKPf + 1], va[4], pb[2][4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) kq[j] = kfrag(j);
+        for (int j = 0; j < kKPf; ++j) kq[j] = kfrag(j);
         va[0] = vfrag(0, 0);
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) pb[0][hb] = pfrag(hb, 0);
 #pragma unroll
         for (int ks = 0; ks < kQk; ++ks) {
           __builtin_amdgcn_sched_barrier(0);   // keep the source order: reads ahead of use
-          if (ks + 2 < kQk) kq[(ks + 2) % 3] = kfrag(ks + 2);
+          if (ks + kKPf < kQk) kq[(ks + kKPf) % (kKPf + 1)] = kfrag(ks + kKPf);
           // Step a runs at ks = 2a + 3.  va[cl] holds token half 0 of column block cl
           // until its last use at ks = 8 cl + 9, then token half 1 (loaded 3 steps later).
           if (ks == 2) va[1] = vfrag(1, 0);
@@ -360,9 +383,9 @@ void attn_partial_h128(const AttnParams p) {
           if (ks == 35) va[3] = vfrag(3, 1);
           if (ks % 4 == 1) copy_row(tn, ks / 4);                                    // ks = 1, 5, .., 33
           if (ks == 0)
-            score_mfma_first(s, kq[ks % 3], qf[ks]);
+            score_mfma_first(s, kq[ks % (kKPf + 1)], qf[ks]);
           else
-            score_mfma(s, kq[ks % 3], qf[ks]);
+            score_mfma(s, kq[ks % (kKPf + 1)], qf[ks]);
           if (ks >= 3 && ks % 2 == 1 && ks < 35) {
             const int a = (ks - 3) / 2;
             acc[a] = mfma32(va[a / 4], pb[0][a % 4], acc[a]);
@@ -407,7 +430,7 @@ void attn_partial_h128(const AttnParams p) {
         l_part += psum;
         // Token half `half` of this lane's probabilities is the B operand (head block
         // `wave`, token half `half`) of the accumulation: store it as is.
-        unsigned char* pout = sm.p[it & 1] + wave * 2 * 1024 + 16 * lane;
+        unsigned char* pout = (unsigned char*)&sm + lo.pb + (it & 1) * kPBuf + wave * 2 * 1024;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           bf16x8 pf;
@@ -435,7 +458,7 @@ void attn_partial_h128(const AttnParams p) {
       }
     };
 
-    run_pass();
+    run_pass(true);
     // A tile above the reference by more than the headroom: every wave learns it and
     // the piece is recomputed with the exact maximum (over both lane halves of each
     // head) as the reference.
@@ -446,10 +469,11 @@ void attn_partial_h128(const AttnParams p) {
     __syncthreads();
     if (redo) {
       m_ref += max_xor32(x_max);
-      run_pass();
+      run_pass(false);
     }
 
     // Epilogue: u = U / l.  Row sums go through LDS to the column-owning waves.
+    const int el = (int)lane_id_opaque(), l32 = el & 31, h = el >> 5;
     const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
     if (h == 0) {
       sm.l[32 * wave + l32] = l_tot;

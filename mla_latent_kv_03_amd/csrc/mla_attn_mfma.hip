@@ -188,7 +188,7 @@ __global__ __launch_bounds__(64 * (HB + kUWaves)) void attn_partial_split(const 
     const int qk_x = l16 & 7;
     const int qk_b0 = l16 * kRowBytes + ((g ^ qk_x) << 4);
     const int qk_b1 = l16 * kRowBytes + (((4 + g) ^ qk_x) << 4);
-    for_each_piece_wave(p.seq_lens, p.batch, p.max_tokens, p.num_splits, w, table, [&](const Piece& pc) {
+    for_each_piece_wave(p.seq_lens, p.batch, p.max_tokens, p.num_splits, w, table, first_lens(p.seq_lens, p.batch, p.max_tokens), [&](const Piece& pc) {
       const PieceInfo pi = piece_info(pc);
       PageWindow pw;
       pw.init(p.block_table + (size_t)pc.b * p.max_pages, p.max_pages, p.num_pages, pi.t0 / p.page_size);
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(64 * (HB + kUWaves)) void attn_partial_split(const 
 #pragma unroll
     for (int cb = 0; cb < kUCb; ++cb)
       tr_base[cb] = uw * kSliceBytes + tr_tok * kRowBytes + (((2 * cb + (tr_q >> 1)) ^ tr_x) << 4) + (tr_q & 1) * 8;
-    for_each_piece_wave(p.seq_lens, p.batch, p.max_tokens, p.num_splits, w, table, [&](const Piece& pc) {
+    for_each_piece_wave(p.seq_lens, p.batch, p.max_tokens, p.num_splits, w, table, first_lens(p.seq_lens, p.batch, p.max_tokens), [&](const Piece& pc) {
       const PieceInfo pi = piece_info(pc);
       PageWindow pw;
       pw.init(p.block_table + (size_t)pc.b * p.max_pages, p.max_pages, p.num_pages, pi.t0 / p.page_size);

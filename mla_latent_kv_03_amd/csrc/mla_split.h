@@ -18,6 +18,7 @@ struct Piece {
   int t0;     // first token (multiple of 64)
   int t1;     // one past the last token (<= L_b)
   int slot;   // partial slot = share + b
+  int len;    // L_b (clamped)
 };
 
 struct SplitScratch {
@@ -106,6 +107,7 @@ __device__ void for_each_piece(const int32_t* __restrict__ seq_lens, int B, int 
       pc.t0 = (int)(u0 * kSplitUnit);
       pc.t1 = (int)(u1 * kSplitUnit < L ? u1 * kSplitUnit : L);
       pc.slot = w + b;
+      pc.len = L;
       pieces[idx] = pc;
     }
     __syncthreads();
@@ -116,12 +118,23 @@ __device__ void for_each_piece(const int32_t* __restrict__ seq_lens, int B, int 
   }
 }
 
+// The lane index from an instruction the compiler cannot look through: addresses built
+// from it are computed where they are used, instead of being hoisted out of loops and
+// kept live (or spilled) across a kernel's main loop.
+__device__ __forceinline__ uint32_t lane_id_opaque() {
+  uint32_t l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ long long wave_inclusive_scan(long long x) {
-  const int lane = threadIdx.x & 63;
+  const int lane = (int)lane_id_opaque();
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const long long y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
+    const int src = (lane >= d ? lane - d : lane) << 2;
+    const unsigned lo = (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)(unsigned)(unsigned long long)x);
+    const unsigned hi = (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)(unsigned)((unsigned long long)x >> 32));
+    if (lane >= d) x += (long long)(((unsigned long long)hi << 32) | lo);
   }
   return x;
 }
@@ -132,65 +145,95 @@ __device__ __forceinline__ long long wave_total(long long x) {
   return x;
 }
 
-// Same walk as for_each_piece, done by each wave on its own (64 sequences per step,
-// wave-level scans, no LDS and no barriers): every wave of a workgroup derives the
-// identical piece list and calls process(piece) in the same order with wave-uniform
-// values.  The wave given a non-null `table` also writes the split-table entries of
-// the sequences b with b % G == w.
+// The clamped length of sequence `lane` (0 past the batch): the first 64 lengths, which
+// a kernel can load before other set-up work and hand to for_each_piece_wave.
+__device__ __forceinline__ int first_lens(const int32_t* __restrict__ seq_lens, int B, int max_tokens) {
+  const int lane = threadIdx.x & 63;
+  return lane < B ? clamp_len(seq_lens[lane], max_tokens) : 0;
+}
+
+// Same rule as for_each_piece, evaluated by each wave on its own (64 sequences per
+// step, wave-level scans, no LDS and no barriers): every wave of a workgroup derives
+// the identical piece list and calls process(piece) in sequence order with
+// wave-uniform values.  The wave given a non-null `table` also writes the split-table
+// entries of the sequences b with b % G == w.  `len0` is first_lens() of the same
+// arguments (sequences 0..63 are then not loaded again).
+//
+// The pieces are found one at a time: each search rescans the lengths and returns the
+// first piece after a scalar cursor, so that no per-lane state of the scan stays live
+// while process() runs (a kernel's main loop then has the vector registers to itself).
 template <class F>
 __device__ void for_each_piece_wave(const int32_t* __restrict__ seq_lens, int B, int max_tokens, int G, int w,
-                                    int32_t* __restrict__ table, F&& process) {
+                                    int32_t* __restrict__ table, int len0, F&& process) {
   const int lane = threadIdx.x & 63;
-  long long total = 0;
-  for (int base = 0; base < B; base += 64) {
+  auto len_of = [&](int base) {
     const int b = base + lane;
-    total += wave_total(b < B ? (clamp_len(seq_lens[b], max_tokens) + kSplitUnit - 1) / kSplitUnit : 0);
-  }
-  if (total == 0) {
-    if (table)
-      for (int b = lane; b < B; b += 64)
-        if (b % G == w) { table[2 * b] = 0; table[2 * b + 1] = 0; }
-    return;
-  }
-  const long long share = (total + G - 1) / G;
+    return base == 0 ? len0 : (b < B ? clamp_len(seq_lens[b], max_tokens) : 0);
+  };
+  // Uniform values are kept in scalar registers.
+  auto uniform64 = [](long long v) {
+    const unsigned lo32 = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long long)v);
+    const unsigned hi32 = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)v >> 32));
+    return (long long)(((unsigned long long)hi32 << 32) | lo32);
+  };
+  long long total = 0;
+  for (int base = 0; base < B; base += 64) total += wave_total((len_of(base) + kSplitUnit - 1) / kSplitUnit);
+  total = uniform64(total);
+  const long long share = total > 0 ? (total + G - 1) / G : 1;
   const long long lo = (long long)w * share;
   const long long hi = lo + share < total ? lo + share : total;
-  long long carry = 0;
-  for (int base = 0; base < B; base += 64) {
-    const int b = base + lane;
-    const int L = b < B ? clamp_len(seq_lens[b], max_tokens) : 0;
-    const long long n = (L + kSplitUnit - 1) / kSplitUnit;
-    const long long incl = wave_inclusive_scan(n);
-    const long long start = carry + incl - n;
-    if (table && b < B && b % G == w) {
-      int first = 0, cnt = 0;
-      if (n > 0) {
-        const long long wf = start / share, wl = (start + n - 1) / share;
-        first = (int)wf + b;
-        cnt = (int)(wl - wf + 1);
+
+  if (table) {
+    long long carry = 0;
+    for (int base = 0; base < B; base += 64) {
+      const int b = base + lane;
+      const long long n = (len_of(base) + kSplitUnit - 1) / kSplitUnit;
+      const long long incl = wave_inclusive_scan(n);
+      const long long start = carry + incl - n;
+      if (b < B && b % G == w) {
+        int first = 0, cnt = 0;
+        if (n > 0) {
+          const long long wf = start / share, wl = (start + n - 1) / share;
+          first = (int)wf + b;
+          cnt = (int)(wl - wf + 1);
+        }
+        table[2 * b] = first;
+        table[2 * b + 1] = cnt;
       }
-      table[2 * b] = first;
-      table[2 * b + 1] = cnt;
+      carry += uniform64(__shfl(incl, 63, 64));
     }
-    const bool mine = n > 0 && start < hi && start + n > lo;
-    const long long u0 = (lo > start ? lo : start) - start;
-    const long long u1 = (hi < start + n ? hi : start + n) - start;
-    const int t0 = (int)(u0 * kSplitUnit);
-    const int t1 = (int)(u1 * kSplitUnit < L ? u1 * kSplitUnit : L);
-    unsigned long long mask = __ballot(mine);
-    while (mask) {
-      const int src = __builtin_ctzll(mask);
-      mask &= mask - 1;
-      Piece pc;
-      pc.b = __builtin_amdgcn_readlane(b, src);
-      pc.t0 = __builtin_amdgcn_readlane(t0, src);
-      pc.t1 = __builtin_amdgcn_readlane(t1, src);
-      pc.slot = w + pc.b;
-      process(pc);
-    }
-    carry += __shfl(incl, 63, 64);
-    if (!table && carry >= hi) break;
   }
+  if (total == 0) return;
+
+  // First piece of share w in a sequence after `after`; false if there is none.
+  auto next_piece = [&](int after, Piece& pc) {
+    long long carry = 0;
+    for (int base = 0; base < B; base += 64) {
+      const int b = base + lane;
+      const int L = len_of(base);
+      const long long n = (L + kSplitUnit - 1) / kSplitUnit;
+      const long long incl = wave_inclusive_scan(n);
+      const long long start = carry + incl - n;
+      const bool mine = b > after && n > 0 && start < hi && start + n > lo;
+      const unsigned long long mask = __ballot(mine);
+      if (mask) {
+        const int src = __builtin_ctzll(mask);
+        const long long u0 = (lo > start ? lo : start) - start;
+        const long long u1 = (hi < start + n ? hi : start + n) - start;
+        pc.b = base + src;
+        pc.t0 = __builtin_amdgcn_readlane((int)(u0 * kSplitUnit), src);
+        pc.t1 = __builtin_amdgcn_readlane((int)(u1 * kSplitUnit < L ? u1 * kSplitUnit : L), src);
+        pc.len = __builtin_amdgcn_readlane(L, src);
+        pc.slot = w + pc.b;
+        return true;
+      }
+      carry += uniform64(__shfl(incl, 63, 64));
+      if (carry >= hi) break;
+    }
+    return false;
+  };
+  Piece pc;
+  for (int after = -1; next_piece(after, pc); after = pc.b) process(pc);
 }
 
 // Block-table entries of one sequence held in registers: lane j of the wave keeps the
@@ -204,16 +247,13 @@ struct PageWindow {
   int base;
   int ids;              // this lane's page id
 
+  // The loaded ids are checked only in get(), so that the load's latency can overlap
+  // whatever the caller issues next.
   __device__ void load(int new_base) {
     base = new_base;
     const int lane = threadIdx.x & 63;
     const int k = base + lane;
-    int id = -1;
-    if (k < max_pages) {
-      id = row[k];
-      if (id < 0 || id >= num_pages) id = -1;
-    }
-    ids = id;
+    ids = k < max_pages ? row[k] : -1;
   }
   __device__ void init(const int32_t* row_, int max_pages_, int num_pages_, int first_page) {
     row = row_;
@@ -221,10 +261,16 @@ struct PageWindow {
     num_pages = num_pages_;
     load(first_page);
   }
+  // Make `page_idx` (at or before the next lookups) readable: reloads the window if it
+  // starts after page_idx, e.g. when a second pass over a piece goes back to its start.
+  __device__ void rewind(int page_idx) {
+    if (page_idx < base) load(page_idx);
+  }
   // page id of logical page `page_idx` (wave-uniform), -1 if invalid
   __device__ int get(int page_idx) {
     if (page_idx >= base + 64) load(page_idx - 32 > base ? page_idx - 32 : base + 32);
-    return __builtin_amdgcn_readlane(ids, page_idx - base);
+    const int id = __builtin_amdgcn_readlane(ids, page_idx - base);
+    return id >= 0 && id < num_pages ? id : -1;
   }
 };
 

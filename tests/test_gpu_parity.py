@@ -147,3 +147,21 @@ def test_late_dominant_token(G):
     o_ref, _ = case.oracle([0, 1])
     tol = dict(rel_l2=BF16_TOL["rel_l2"], max_abs=max(BF16_TOL["max_abs"], 2.0 ** -7 * float(np.abs(o_ref).max())))
     compare_sampled(case, out, lse, [0, 1], tol, lse_tol=5e-3, what="late dominant token")
+
+
+def test_late_dominant_token_long_piece():
+    """One piece of 94 pages (a single split): the page-id window slides forward during
+    the first pass, the dominant token at position 5500 forces a second pass, and that
+    pass must start again from the piece's first pages."""
+    _print_case("late_dominant_token_long_piece", G=1)
+    import torch
+    x = workloads.make_decode([6000], n_h=128, page_size=64, seed=78)
+    qdir = torch.sign(x.q_nope[0, 0].float().mean(dim=0))
+    t = 5500
+    slot = int(x.block_table[0, t // x.page_size]) * x.page_size + t % x.page_size
+    x.pool[slot, :x.d_c] = (30.0 * qdir).to(x.pool.dtype)
+    case = DeviceCase(x, num_splits=1)
+    out, lse, _ = case.run()
+    o_ref, _ = case.oracle([0])
+    tol = dict(rel_l2=BF16_TOL["rel_l2"], max_abs=max(BF16_TOL["max_abs"], 2.0 ** -7 * float(np.abs(o_ref).max())))
+    compare_sampled(case, out, lse, [0], tol, lse_tol=5e-3, what="late dominant token, long piece")
