@@ -145,12 +145,45 @@ class Resident:
         return sum(t.numel() * t.element_size() for t in (self.pool, self.q_nope, self.q_pe, self.workspace))
 
 
+def hip_runtime():
+    """The HIP runtime library torch is using (for events the C library records itself)."""
+    import ctypes
+    import torch  # noqa: F401  (loads libamdhip64)
+    hip = ctypes.CDLL("libamdhip64.so", mode=ctypes.RTLD_GLOBAL)
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def hip_event_create(hip):
+    import ctypes
+    ev = ctypes.c_void_p()
+    if hip.hipEventCreate(ctypes.byref(ev)) != 0:
+        raise RuntimeError("hipEventCreate failed")
+    return ev
+
+
+def hip_elapsed_ms(hip, start, stop):
+    import ctypes
+    ms = ctypes.c_float()
+    rc = hip.hipEventElapsedTime(ctypes.byref(ms), start, stop)
+    if rc != 0:
+        raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+    return ms.value
+
+
 def step(r, ev=None):
+    """One step: append, partial attention, combine.  ev = (stream events e0..e3 around the three
+    calls, kernel events k0, k1): k0/k1 are recorded by the attention kernel itself at its start
+    and end (mla_set_attention_events), so its duration excludes the dispatch gap that the stream
+    events around the call include."""
     if ev is not None:
         ev[0].record()
     rc = r.lib.mla_paged_cache_append(*r.append_args)
     if ev is not None:
         ev[1].record()
+        rc |= r.lib.mla_set_attention_events(ev[6], ev[7])
     rc |= r.lib.mla_decode_fwd(*r.fwd_args)                 # out = NULL: partial attention only
     if ev is not None:
         ev[2].record()
@@ -307,19 +340,32 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Kernel events: recorded by the library (not by torch), so they are created and read
+    # through the HIP runtime that torch has loaded.
+    hip = hip_runtime()
+    evs = []
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] + [None, None]
+        k = [hip_event_create(hip), hip_event_create(hip)]
+        evs.append(e + k)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(copies[i % n_copies], evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    binding.mla_set_attention_events(None, None)
     ms_step = wall * 1e3 / args.steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    attn_ms = sum(hip_elapsed_ms(hip, e[6], e[7]) for e in evs) / args.steps
+    for e in evs:
+        hip.hipEventDestroy(e[6])
+        hip.hipEventDestroy(e[7])
+    attn_call_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     comb_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
     app_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     print(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step; append {app_ms * 1e3:.1f} us, "
-          f"attention {attn_ms * 1e3:.1f} us, combine {comb_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+          f"attention kernel {attn_ms * 1e3:.1f} us (call incl. dispatch {attn_call_ms * 1e3:.1f} us), "
+          f"combine {comb_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     alg = algorithmic(x)
     kname, ksrc = attn_kernel(x)

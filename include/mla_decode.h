@@ -180,6 +180,17 @@ mla_status_t mla_paged_cache_append(const mla_decode_params_t* params, const voi
                                     const int32_t* positions, const int32_t* block_table, void* c_kv,
                                     void* k_pe, float* kv_scale, void* stream);
 
+/*
+ * Measurement hook (for callers that time the attention kernel, such as a benchmark):
+ * the partial-attention kernel of every later mla_decode_fwd call made by the calling
+ * thread records `start` when it begins executing and `stop` when it ends (hipEvent_t
+ * handles created by the caller, which keeps ownership).  Unlike events recorded on
+ * the stream around the call, these exclude the dispatch gap before the kernel.
+ * NULL, NULL restores plain launches.  The setting is per thread; it does not touch
+ * the append or combine kernels.  Always returns MLA_OK.
+ */
+mla_status_t mla_set_attention_events(void* start, void* stop);
+
 /* Static description of a status code. */
 const char* mla_status_string(mla_status_t status);
 

@@ -19,7 +19,7 @@ _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE", 4: "MLA_ERR_WORKSPACE",
           5: "MLA_ERR_HIP", 6: "MLA_ERR_UNSUPPORTED"}
 EXPORTS = ("mla_decode_num_splits", "mla_decode_workspace_size", "mla_decode_fwd", "mla_decode_splitkv_combine",
-           "mla_paged_cache_append", "mla_status_string", "mla_abi_version")
+           "mla_paged_cache_append", "mla_set_attention_events", "mla_status_string", "mla_abi_version")
 
 
 class DecodeParams(ctypes.Structure):
@@ -59,6 +59,8 @@ def _load():
     lib.mla_decode_splitkv_combine.restype = ctypes.c_int
     lib.mla_paged_cache_append.argtypes = [P, vp, vp, ctypes.c_int32, ctypes.c_int, i32p, i32p, vp, vp, f32p, vp]
     lib.mla_paged_cache_append.restype = ctypes.c_int
+    lib.mla_set_attention_events.argtypes = [vp, vp]
+    lib.mla_set_attention_events.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
@@ -172,6 +174,13 @@ def mla_paged_cache_append(params, c_new, k_pe_new, positions, block_table, c_kv
                                       _DTYPE_CODE[c_new.dtype], _ptr(positions), _ptr(block_table), _ptr(c_kv),
                                       _ptr(k_pe), _ptr(kv_scale), _stream())
     _check(code, "mla_paged_cache_append")
+
+
+def mla_set_attention_events(start=None, stop=None):
+    """Record torch.cuda.Event `start` / `stop` at the beginning and end of the partial-attention
+    kernel of this thread's later mla_decode_fwd calls (None, None: plain launches)."""
+    h = lambda e: ctypes.c_void_p(e.cuda_event) if e is not None else None
+    _check(LIB.mla_set_attention_events(h(start), h(stop)), "mla_set_attention_events")
 
 
 def workspace_views(params, workspace):

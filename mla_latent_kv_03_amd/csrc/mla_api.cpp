@@ -143,9 +143,23 @@ mla_status_t combine_impl(const mla_decode_params_t& p, int G, const void* works
 
 }  // namespace
 
+namespace mla {
+AttentionEvents& attention_events() {
+  static thread_local AttentionEvents ev;
+  return ev;
+}
+}  // namespace mla
+
 extern "C" {
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+mla_status_t mla_set_attention_events(void* start, void* stop) {
+  mla::AttentionEvents& ev = mla::attention_events();
+  ev.start = static_cast<hipEvent_t>(start);
+  ev.stop = static_cast<hipEvent_t>(stop);
+  return MLA_OK;
+}
 
 const char* mla_status_string(mla_status_t s) {
   switch (s) {

@@ -119,8 +119,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(const AttnParams p)
 
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream) {
   dim3 grid(p.num_splits, p.s_q * p.n_h);
-  hipLaunchKernelGGL(attn_partial_f32, grid, dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  return launch_attention_kernel(attn_partial_f32, grid, dim3(kThreads), stream, p);
 }
 
 }  // namespace mla

@@ -281,8 +281,7 @@ hipError_t launch_attn_fp8_v0(const AttnParams& p, hipStream_t stream) {
   const int row_groups = rows / p.rows_per_group;
   dim3 grid(p.num_splits, row_groups);
   dim3 block(64 * (p.rows_per_group / 16));
-  hipLaunchKernelGGL(attn_partial_mfma<true>, grid, block, 0, stream, p);
-  return hipGetLastError();
+  return launch_attention_kernel(attn_partial_mfma<true>, grid, block, stream, p);
 }
 
 }  // namespace mla

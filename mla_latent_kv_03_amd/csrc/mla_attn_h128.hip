@@ -507,8 +507,7 @@ void attn_partial_h128(const AttnParams p) {
 hipError_t launch_attn_h128(const AttnParams& p, hipStream_t stream) {
   if (p.n_h % kHeads != 0 || p.d_c != kDc || p.d_r != kDr) return hipErrorInvalidValue;
   dim3 grid(p.num_splits, p.s_q * (p.n_h / kHeads));
-  hipLaunchKernelGGL(attn_partial_h128, grid, dim3(64 * kWaves), 0, stream, p);
-  return hipGetLastError();
+  return launch_attention_kernel(attn_partial_h128, grid, dim3(64 * kWaves), stream, p);
 }
 
 }  // namespace mla

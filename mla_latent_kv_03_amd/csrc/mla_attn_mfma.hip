@@ -433,10 +433,8 @@ hipError_t launch_attn_mfma(const AttnParams& p, bool fp8, hipStream_t stream) {
   dim3 block(64 * (HB + kUWaves));
   const bool packed = p.packed_rows != 0;
 #define MLA_LAUNCH(hb)                                                                          \
-  if (packed)                                                                                   \
-    hipLaunchKernelGGL((attn_partial_split<hb, true>), grid, block, 0, stream, p);              \
-  else                                                                                          \
-    hipLaunchKernelGGL((attn_partial_split<hb, false>), grid, block, 0, stream, p);
+  return packed ? launch_attention_kernel(attn_partial_split<hb, true>, grid, block, stream, p)  \
+                : launch_attention_kernel(attn_partial_split<hb, false>, grid, block, stream, p);
   switch (HB) {
     case 1: MLA_LAUNCH(1) break;
     case 2: MLA_LAUNCH(2) break;

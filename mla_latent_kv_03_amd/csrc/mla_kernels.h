@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace mla {
@@ -56,6 +57,24 @@ struct AppendParams {
 
 // Heads of one query position handled by one workgroup of the bf16 kernel.
 int attn_heads_per_group(int n_h);
+// Start/stop events for the partial-attention kernel of the calling thread's next
+// launches (null: a plain launch).  Set through mla_set_attention_events; used only to
+// time the kernel itself, excluding the dispatch gap a stream event would include.
+struct AttentionEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+AttentionEvents& attention_events();
+
+template <class Kernel, class... Args>
+hipError_t launch_attention_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  const AttentionEvents& ev = attention_events();
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_mfma(const AttnParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_attn_h128(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_fp8_v0(const AttnParams& p, hipStream_t stream);
