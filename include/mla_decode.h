@@ -101,8 +101,10 @@ typedef struct {
  * Workspace layout (all offsets from the workspace base, each 256-byte aligned):
  *   split_table  int32 [B][2]                     (first slot, count) per sequence; (0, 0) if L_b = 0
  *   partial_lse  float [num_slots][s_q][n_h]      ln-sum-exp of the piece's scores; -inf if empty
- *   partial_u    float [num_slots][s_q][n_h][d_c] u of the piece, normalized by its own softmax sum
- * with num_slots = G + B.  Rows of a piece that see no token have lse = -inf and u = 0.
+ *   partial_u    E     [num_slots][s_q][n_h][d_c] u of the piece, normalized by its own softmax sum
+ * with num_slots = G + B and E = float for the fp32 dtype combination, bf16 (round to
+ * nearest even) for the bf16 and E4M3-cache combinations, whose output is bf16 anyway.
+ * Rows of a piece that see no token have lse = -inf and u = 0.
  */
 
 /* Effective number of splits G for these params on the current device

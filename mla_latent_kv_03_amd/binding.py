@@ -193,5 +193,7 @@ def workspace_views(params, workspace):
     off_u = off_lse + a256(slots * s_q * n_h * 4)
     table = workspace[: B * 8].view(torch.int32).view(B, 2)
     plse = workspace[off_lse: off_lse + slots * s_q * n_h * 4].view(torch.float32).view(slots, s_q, n_h)
-    pu = workspace[off_u: off_u + slots * s_q * n_h * d_c * 4].view(torch.float32).view(slots, s_q, n_h, d_c)
+    u_dtype = torch.float32 if params.q_dtype == F32 else torch.bfloat16   # the header's element type E
+    u_size = torch.finfo(u_dtype).bits // 8
+    pu = workspace[off_u: off_u + slots * s_q * n_h * d_c * u_size].view(u_dtype).view(slots, s_q, n_h, d_c)
     return table, plse, pu

@@ -113,7 +113,9 @@ Layout layout_of(const mla_decode_params_t& p, int G) {
   l.table = 0;
   l.lse = align256((size_t)p.batch * 2 * sizeof(int32_t));
   l.u = l.lse + align256(rows * sizeof(float));
-  l.total = l.u + align256(rows * (size_t)p.d_c * sizeof(float));
+  // partial_u: float32 on the fp32 path, bf16 on the bf16 / E4M3-cache paths.
+  const size_t u_elem = path_of(p) == Path::kF32 ? sizeof(float) : 2;
+  l.total = l.u + align256(rows * (size_t)p.d_c * u_elem);
   return l;
 }
 
@@ -127,7 +129,7 @@ mla_status_t combine_impl(const mla_decode_params_t& p, int G, const void* works
   mla::CombineParams c;
   c.split_table = (const int32_t*)((const char*)workspace + l.table);
   c.part_lse = (const float*)((const char*)workspace + l.lse);
-  c.part_u = (const float*)((const char*)workspace + l.u);
+  c.part_u = (const char*)workspace + l.u;
   c.w_uv = w_uv;
   c.out = out;
   c.lse = lse;
@@ -236,7 +238,7 @@ mla_status_t mla_decode_fwd(const mla_decode_params_t* params, const void* q_nop
   a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
   a.split_table = (int32_t*)((char*)workspace + l.table);
   a.part_lse = (float*)((char*)workspace + l.lse);
-  a.part_u = (float*)((char*)workspace + l.u);
+  a.part_u = (char*)workspace + l.u;
   hipError_t e = path == Path::kF32 ? mla::launch_attn_f32(a, s) : mla::launch_attn_mfma(a, path == Path::kFp8, s);
   if (e != hipSuccess) return MLA_ERR_HIP;
   if (!out) return MLA_OK;

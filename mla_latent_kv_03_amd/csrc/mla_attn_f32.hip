@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(const AttnParams p)
 #pragma unroll
     for (int i = 0; i < kColsPerThread; ++i) {
       const int k = tid + i * kThreads;
-      if (k < p.d_c) p.part_u[orow * p.d_c + k] = u[i] * inv;
+      if (k < p.d_c) ((float*)p.part_u)[orow * p.d_c + k] = u[i] * inv;
     }
     __syncthreads();
   });

@@ -267,9 +267,9 @@ __global__ __launch_bounds__(kMaxThreads) void attn_partial_mfma(const AttnParam
     const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     const size_t orow = ((size_t)slot * p.s_q + q_pos) * p.n_h + head0 + l16;
     if (g == 0) p.part_lse[orow] = lse;
-    float* up = p.part_u + orow * kDc + 4 * g;
+    bf16* up = (bf16*)p.part_u + orow * kDc + 4 * g;
 #pragma unroll
-    for (int cb = 0; cb < kCb; ++cb) *(f32x4*)(up + cb * 16) = U[cb] * inv;
+    for (int cb = 0; cb < kCb; ++cb) *(bf16x4*)(up + cb * 16) = to_bf16x4(U[cb] * inv);
     __syncthreads();
   });
 }

@@ -484,7 +484,7 @@ void attn_partial_h128(const AttnParams p) {
     for (int hb = 0; hb < 4; ++hb) {
       const float lt = sm.l[32 * hb + l32];
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      float* up = p.part_u + (row_base + 32 * hb + l32) * kDc + 128 * wave + 4 * h;
+      bf16* up = (bf16*)p.part_u + (row_base + 32 * hb + l32) * kDc + 128 * wave + 4 * h;
 #pragma unroll
       for (int cl = 0; cl < 4; ++cl)
 #pragma unroll
@@ -493,7 +493,7 @@ void attn_partial_h128(const AttnParams p) {
           f32x4 o;
 #pragma unroll
           for (int k = 0; k < 4; ++k) o[k] = acc[4 * cl + hb][4 * g4 + k] * inv;
-          *(f32x4*)(up + 32 * cl + 8 * g4) = o;
+          *(bf16x4*)(up + 32 * cl + 8 * g4) = to_bf16x4(o);
         }
     }
     // The next piece's prologue refills ring slots 0 and 1 and the row sums, which other

@@ -411,9 +411,9 @@ __global__ __launch_bounds__(64 * (HB + kUWaves)) void attn_partial_split(const 
       }
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        float* up = p.part_u + (pi.row_base + hb * 16 + l16) * kDc + uw * 64 + 4 * g;
+        bf16* up = (bf16*)p.part_u + (pi.row_base + hb * 16 + l16) * kDc + uw * 64 + 4 * g;
 #pragma unroll
-        for (int cb = 0; cb < kUCb; ++cb) *(f32x4*)(up + cb * 16) = acc[cb][hb] * inv[hb];
+        for (int cb = 0; cb < kUCb; ++cb) *(bf16x4*)(up + cb * 16) = to_bf16x4(acc[cb][hb] * inv[hb]);
       }
       __syncthreads();
     });

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const 
   const int nrows = min(RB, R - row0);
   const int part = wave % P;
   const size_t step = (size_t)p.s_q * p.n_h;                 // partial rows per slot
-  const size_t slot_bytes = step * kDc * sizeof(float);
+  const size_t slot_bytes = step * kDc * sizeof(bf16);
   auto unit_of = [&](int m) { return P > 1 ? wave / P : wave + kCombineWaves * m; };
 
   // Split-table entries of this wave's units: lane m holds unit m's (first, count).
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const 
     int row, half, cnt;
     size_t base;   // partial row of the unit's first slot
     float l;
-    f32x4 v[kS];
+    bf16x4 v[kS];
   };
   auto start = [&](int m, Unit& st) {
     const int u = unit_of(m);
@@ -95,11 +95,11 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const 
     st.cnt = st.row < nrows ? count : 0;
     st.base = ((size_t)first * p.s_q + (row0 + st.row) % p.s_q) * p.n_h + head;
     st.l = lane < st.cnt ? p.part_lse[st.base + lane * step] : -INFINITY;
-    const char* src = (const char*)(p.part_u + st.base * kDc + 256 * st.half) + 16 * lane;
+    const char* src = (const char*)((const bf16*)p.part_u + st.base * kDc + 256 * st.half) + 8 * lane;
 #pragma unroll
     for (int k = 0; k < kS; ++k) {
       const int s = part + P * k;
-      if (s < st.cnt) st.v[k] = __builtin_nontemporal_load((const f32x4*)(src + (size_t)s * slot_bytes));
+      if (s < st.cnt) st.v[k] = __builtin_nontemporal_load((const bf16x4*)(src + (size_t)s * slot_bytes));
     }
   };
   // Merge one unit: weights w_s = exp(lse_s - lse) for slot = lane (64 at a time), the
@@ -138,21 +138,21 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const 
 #pragma unroll
     for (int k = 0; k < kS; ++k) {
       const int s = part + P * k;
-      if (s < cnt) acc += weight(s) * st.v[k];
+      if (s < cnt) acc += weight(s) * from_bf16x4(st.v[k]);
     }
     // Slots past the first kS of this wave: further batches of kS loads.
-    const char* src = (const char*)(p.part_u + st.base * kDc + 256 * st.half) + 16 * lane;
+    const char* src = (const char*)((const bf16*)p.part_u + st.base * kDc + 256 * st.half) + 8 * lane;
     for (int j0 = kS; part + P * j0 < cnt; j0 += kS) {
-      f32x4 v[kS];
+      bf16x4 v[kS];
 #pragma unroll
       for (int k = 0; k < kS; ++k) {
         const int s = part + P * (j0 + k);
-        if (s < cnt) v[k] = __builtin_nontemporal_load((const f32x4*)(src + (size_t)s * slot_bytes));
+        if (s < cnt) v[k] = __builtin_nontemporal_load((const bf16x4*)(src + (size_t)s * slot_bytes));
       }
 #pragma unroll
       for (int k = 0; k < kS; ++k) {
         const int s = part + P * (j0 + k);
-        if (s < cnt) acc += weight(s) * v[k];
+        if (s < cnt) acc += weight(s) * from_bf16x4(v[k]);
       }
     }
     return acc;
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void combine_upproj_f32(const CombineParams p)
       for (int s = 0; s < count; ++s) {
         const size_t prow = ((size_t)(first + s) * p.s_q + q) * p.n_h + head;
         const float l = p.part_lse[prow];
-        if (l != -INFINITY) acc = fmaf(expf(l - mx) * inv, p.part_u[prow * p.d_c + k], acc);
+        if (l != -INFINITY) acc = fmaf(expf(l - mx) * inv, ((const float*)p.part_u)[prow * p.d_c + k], acc);
       }
       u_s[rr][k] = acc;
     }

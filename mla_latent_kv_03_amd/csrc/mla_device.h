@@ -76,6 +76,17 @@ __device__ __forceinline__ bf16x2 pack_bf16(float a, float b) {
   return __builtin_convertvector(v, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
 }
 
+// Four floats to bf16, round to nearest even.
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
+  const bf16x2 a = pack_bf16(v[0], v[1]), b = pack_bf16(v[2], v[3]);
+  return bf16x4{a[0], a[1], b[0], b[1]};
+}
+
+// Four bf16 to float (exact).
+__device__ __forceinline__ f32x4 from_bf16x4(bf16x4 v) {
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }

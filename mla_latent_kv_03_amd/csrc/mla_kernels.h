@@ -25,14 +25,14 @@ struct AttnParams {
   float scale_log2;          // softmax_scale * log2(e)
   int32_t* split_table;      // [B][2]
   float* part_lse;           // [G + B][s_q][n_h]
-  float* part_u;             // [G + B][s_q][n_h][d_c]
+  void* part_u;              // [G + B][s_q][n_h][d_c]: bf16 (bf16 / E4M3 caches) or float32 (fp32 path)
 };
 
 // Arguments of the combine + up-projection kernels.
 struct CombineParams {
   const int32_t* split_table;
   const float* part_lse;
-  const float* part_u;
+  const void* part_u;        // bf16 for combine_upproj_bf16, float32 for the fp32 path
   const void* w_uv;          // [n_h, d_v, d_c]
   void* out;                 // [B, s_q, n_h, d_v]
   float* lse;                // [B, s_q, n_h] or null

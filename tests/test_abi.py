@@ -55,8 +55,14 @@ def test_workspace_size_matches_header_layout(b):
     a256 = lambda x: (x + 255) // 256 * 256
     slots = 16 + 5
     rows = slots * 2 * 128
-    assert b.mla_decode_workspace_size(p) == a256(5 * 8) + a256(rows * 4) + a256(rows * 512 * 4)
+    # bf16 params: partial_u holds bf16
+    assert b.mla_decode_workspace_size(p) == a256(5 * 8) + a256(rows * 4) + a256(rows * 512 * 2)
     assert b.mla_decode_num_splits(p) == 16
+    # fp32 params: partial_u holds float32
+    pf = b.make_params(batch=3, s_q=1, n_h=8, d_c=64, d_r=16, d_v=16, page_size=64, num_pages=10, max_pages_per_seq=4,
+                       c_kv_stride=80, k_pe_stride=80, softmax_scale=0.1, q_dtype=b.F32, kv_dtype=b.F32, num_splits=4)
+    rows_f = (4 + 3) * 1 * 8
+    assert b.mla_decode_workspace_size(pf) == a256(3 * 8) + a256(rows_f * 4) + a256(rows_f * 64 * 4)
 
 
 FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced: validation fails first

@@ -29,7 +29,7 @@ def test_partials_and_split_table(kv):
     want_table, pieces = ref.split_table(lens, G)
     assert np.array_equal(table.cpu().numpy(), want_table), "split table differs"
     qn, qp = x.q_nope.double().numpy(), x.q_pe.double().numpy()
-    plse_h, pu_h = plse.cpu().numpy(), pu.cpu().numpy()
+    plse_h, pu_h = plse.cpu().numpy(), pu.float().cpu().numpy()
     tol = F32_TOL if kv == "f32" else BF16_TOL
     for (b, w, slot, t0, t1) in pieces:
         c, kp = case.rows_of(b)
