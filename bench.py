@@ -54,8 +54,11 @@ WORKLOADS = ("v3_decode_b64_l4096", "v3_paged_b128", "v3_mtp_b32_l32768", "v3_lo
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--min-warmup-ms", type=float, default=250.0,
+                    help="keep running untimed warmup steps (after the first W) until this much wall time has "
+                         "passed: the GPU's clocks settle only under sustained load")
     ap.add_argument("--workload", default=WORKLOADS[0], choices=WORKLOADS)
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -132,12 +135,12 @@ class Resident:
         P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         self.lib = binding.LIB
-        self.append_args = (ctypes.byref(self.params), P(self.new_c), P(self.new_k), 1,
-                            binding._DTYPE_CODE[self.new_c.dtype], P(self.positions), P(self.block_table),
-                            P(self.c_kv), P(self.k_pe), P(self.kv_scale), stream)
-        self.fwd_args = (ctypes.byref(self.params), P(self.q_nope), P(self.q_pe), P(self.c_kv), P(self.k_pe),
-                         P(self.kv_scale), P(self.block_table), P(self.seq_lens), P(self.w_uv), None, None,
-                         P(self.workspace), self.workspace.numel(), stream)
+        # append + partial attention in one call (one launch on the 128-head bf16 path)
+        self.fwd_append_args = (ctypes.byref(self.params), P(self.new_c), P(self.new_k), 1,
+                                binding._DTYPE_CODE[self.new_c.dtype], P(self.positions), P(self.q_nope),
+                                P(self.q_pe), P(self.c_kv), P(self.k_pe), P(self.kv_scale), P(self.block_table),
+                                P(self.seq_lens), P(self.w_uv), None, None, P(self.workspace),
+                                self.workspace.numel(), stream)
         self.comb_args = (ctypes.byref(self.params), P(self.workspace), self.workspace.numel(), P(self.w_uv),
                           P(self.out), P(self.lse), stream)
 
@@ -174,17 +177,17 @@ def hip_elapsed_ms(hip, start, stop):
 
 
 def step(r, ev=None):
-    """One step: append, partial attention, combine.  ev = (stream events e0..e3 around the three
-    calls, kernel events k0, k1): k0/k1 are recorded by the attention kernel itself at its start
-    and end (mla_set_attention_events), so its duration excludes the dispatch gap that the stream
-    events around the call include."""
+    """One step: append + partial attention (mla_decode_fwd_append, out = NULL), then the combine
+    and up-projection (mla_decode_splitkv_combine).  ev = (stream events e0..e3 around the calls,
+    kernel events k0, k1): k0/k1 are recorded by the attention kernel itself at its start and end
+    (mla_set_attention_events), so its duration excludes the dispatch gap that the stream events
+    around the call include."""
+    rc = 0
     if ev is not None:
         ev[0].record()
-    rc = r.lib.mla_paged_cache_append(*r.append_args)
-    if ev is not None:
         ev[1].record()
         rc |= r.lib.mla_set_attention_events(ev[6], ev[7])
-    rc |= r.lib.mla_decode_fwd(*r.fwd_args)                 # out = NULL: partial attention only
+    rc |= r.lib.mla_decode_fwd_append(*r.fwd_append_args)
     if ev is not None:
         ev[2].record()
     rc |= r.lib.mla_decode_splitkv_combine(*r.comb_args)
@@ -327,9 +330,15 @@ def main():
     G = binding.mla_decode_num_splits(first.params)
     print(f"[bench] {n_copies} resident copies of {first.nbytes() / 1e6:.1f} MB, G={G}", file=sys.stderr, flush=True)
 
-    for i in range(args.warmup):
+    t_w = time.perf_counter()
+    i = 0
+    while i < args.warmup or (time.perf_counter() - t_w) * 1e3 < args.min_warmup_ms:
         step(copies[i % n_copies])
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    n_warm = i
     if args.copy_calibration_mb:
         # a plain streaming kernel of known traffic (reads and writes n bytes): torch's negation
         n = args.copy_calibration_mb * 2 ** 20
@@ -371,9 +380,8 @@ def main():
         hip.hipEventDestroy(e[7])
     attn_call_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     comb_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-    app_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    print(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step; with events: append {app_ms * 1e3:.1f} us, "
-          f"attention kernel {attn_ms * 1e3:.1f} us (call incl. dispatch {attn_call_ms * 1e3:.1f} us), "
+    print(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step; with events: attention kernel "
+          f"{attn_ms * 1e3:.1f} us (append + attention call incl. dispatch {attn_call_ms * 1e3:.1f} us), "
           f"combine {comb_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     alg = algorithmic(x)
@@ -399,7 +407,9 @@ def main():
         "config": {"workload": args.workload, "batch": x.batch, "s_q": x.s_q, "n_h": x.n_h, "d_c": x.d_c,
                    "d_r": x.d_r, "d_v": x.d_v, "context": int(x.seq_lens.max()),
                    "cached_tokens_per_step": alg["tokens"], "kv_dtype": x.kv_dtype, "page_size": x.page_size,
-                   "num_splits": G, "step": "append + partial attention + combine/up-projection",
+                   "num_splits": G, "step": "append + partial attention (one call, mla_decode_fwd_append) + "
+                                            "combine/up-projection (mla_decode_splitkv_combine)",
+                   "warmup_steps_run": n_warm,
                    "hbm_gbs_whole_step": round(alg["total_bytes"] / (ms_step * 1e-3) / 1e9, 1)},
         "roofline": roof,
     }

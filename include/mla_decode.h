@@ -183,6 +183,23 @@ mla_status_t mla_paged_cache_append(const mla_decode_params_t* params, const voi
                                     void* k_pe, float* kv_scale, void* stream);
 
 /*
+ * Append, then decode: the same effect as mla_paged_cache_append(params, c_new, k_pe_new,
+ * s_new, in_dtype, positions, block_table, c_kv, k_pe, kv_scale) followed by
+ * mla_decode_fwd(params, q_nope, ..., stream) on the same stream (arguments and
+ * validation as there; nothing is launched unless both would be accepted).
+ * When the cache and the new rows are bf16, n_h is a multiple of 128 and s_new <= 2,
+ * both happen in the one partial-attention launch: tiles that hold a new position take
+ * that row from c_new / k_pe_new, and the pool rows are written at the end of the
+ * launch.  The outputs and the pool afterwards are the same bits as with the two calls.
+ * Otherwise the two calls are made.
+ */
+mla_status_t mla_decode_fwd_append(const mla_decode_params_t* params, const void* c_new, const void* k_pe_new,
+                                   int32_t s_new, mla_dtype_t in_dtype, const int32_t* positions,
+                                   const void* q_nope, const void* q_pe, void* c_kv, void* k_pe, float* kv_scale,
+                                   const int32_t* block_table, const int32_t* seq_lens, const void* w_uv,
+                                   void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Measurement hook (for callers that time the attention kernel, such as a benchmark):
  * the partial-attention kernel of every later mla_decode_fwd call made by the calling
  * thread records `start` when it begins executing and `stop` when it ends (hipEvent_t

@@ -7,7 +7,7 @@ first use; a missing or incomplete libmla_decode.so raises ImportError.
 ``workloads`` holds the seeded synthetic inputs.
 """
 _EXPORTS = ("mla_decode_fwd", "mla_decode_splitkv_combine", "mla_paged_cache_append",
-            "mla_decode_workspace_size", "mla_decode_num_splits", "mla_set_attention_events", "params_for", "make_params",
+            "mla_decode_workspace_size", "mla_decode_num_splits", "mla_decode_fwd_append", "mla_set_attention_events", "params_for", "make_params",
             "workspace_views", "MLAError")
 
 

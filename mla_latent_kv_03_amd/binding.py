@@ -19,7 +19,8 @@ _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE", 4: "MLA_ERR_WORKSPACE",
           5: "MLA_ERR_HIP", 6: "MLA_ERR_UNSUPPORTED"}
 EXPORTS = ("mla_decode_num_splits", "mla_decode_workspace_size", "mla_decode_fwd", "mla_decode_splitkv_combine",
-           "mla_paged_cache_append", "mla_set_attention_events", "mla_status_string", "mla_abi_version")
+           "mla_paged_cache_append", "mla_decode_fwd_append", "mla_set_attention_events", "mla_status_string",
+           "mla_abi_version")
 
 
 class DecodeParams(ctypes.Structure):
@@ -59,6 +60,9 @@ def _load():
     lib.mla_decode_splitkv_combine.restype = ctypes.c_int
     lib.mla_paged_cache_append.argtypes = [P, vp, vp, ctypes.c_int32, ctypes.c_int, i32p, i32p, vp, vp, f32p, vp]
     lib.mla_paged_cache_append.restype = ctypes.c_int
+    lib.mla_decode_fwd_append.argtypes = [P, vp, vp, ctypes.c_int32, ctypes.c_int, i32p, vp, vp, vp, vp, f32p, i32p,
+                                          i32p, vp, vp, f32p, vp, ctypes.c_size_t, vp]
+    lib.mla_decode_fwd_append.restype = ctypes.c_int
     lib.mla_set_attention_events.argtypes = [vp, vp]
     lib.mla_set_attention_events.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -157,6 +161,32 @@ def mla_decode_fwd(q_nope, q_pe, c_kv, k_pe, block_table, seq_lens, w_uv, *, sof
                               _ptr(kv_scale), _ptr(block_table), _ptr(seq_lens), _ptr(w_uv), _ptr(out), _ptr(lse),
                               _ptr(workspace), workspace.numel(), _stream())
     _check(code, "mla_decode_fwd")
+    return out, lse, workspace
+
+
+def mla_decode_fwd_append(c_new, k_pe_new, positions, q_nope, q_pe, c_kv, k_pe, block_table, seq_lens, w_uv, *,
+                          softmax_scale, page_size, kv_scale=None, num_splits=0, out=None, lse=None, workspace=None,
+                          partials_only=False, params=None):
+    """mla_paged_cache_append of the new rows ([B, s_new, d]) at `positions`, then mla_decode_fwd, in
+    one call (one launch on the 128-head bf16 path); returns (out, lse, workspace)."""
+    if params is None:
+        params = params_for(q_nope, q_pe, c_kv, k_pe, block_table, w_uv, softmax_scale=softmax_scale,
+                            page_size=page_size, num_splits=num_splits)
+    dev = q_nope.device
+    if workspace is None:
+        workspace = alloc_workspace(params, dev)
+    if not partials_only:
+        if out is None:
+            out = torch.empty(q_nope.shape[:3] + (w_uv.shape[1],), dtype=q_nope.dtype, device=dev)
+        if lse is None:
+            lse = torch.empty(q_nope.shape[:3], dtype=torch.float32, device=dev)
+    else:
+        out, lse = None, None
+    code = LIB.mla_decode_fwd_append(ctypes.byref(params), _ptr(c_new), _ptr(k_pe_new), int(c_new.shape[1]),
+                                     _DTYPE_CODE[c_new.dtype], _ptr(positions), _ptr(q_nope), _ptr(q_pe), _ptr(c_kv),
+                                     _ptr(k_pe), _ptr(kv_scale), _ptr(block_table), _ptr(seq_lens), _ptr(w_uv),
+                                     _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
+    _check(code, "mla_decode_fwd_append")
     return out, lse, workspace
 
 

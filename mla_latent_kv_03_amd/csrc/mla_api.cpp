@@ -143,6 +143,110 @@ mla_status_t combine_impl(const mla_decode_params_t& p, int G, const void* works
   return launch_status(mla::launch_combine_bf16(c, stream));
 }
 
+mla_status_t prepare_fwd(const mla_decode_params_t* params, const void* q_nope, const void* q_pe, const void* c_kv,
+                         const void* k_pe, const float* kv_scale, const int32_t* block_table,
+                         const int32_t* seq_lens, const void* w_uv, void* workspace, size_t workspace_bytes,
+                         mla::AttnParams& a, int& G) {
+  mla_status_t st = check_common(params);
+  if (st != MLA_OK) return st;
+  const mla_decode_params_t& p = *params;
+  const Path path = path_of(p);
+  if (!q_nope || !q_pe || !c_kv || !block_table || !seq_lens || !w_uv) return MLA_ERR_NULL;
+  if (p.d_r > 0 && !k_pe) return MLA_ERR_NULL;
+  if ((path == Path::kFp8) != (kv_scale != nullptr)) return path == Path::kFp8 ? MLA_ERR_NULL : MLA_ERR_DTYPE;
+  if (path != Path::kF32) {
+    if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(c_kv) || !aligned16(k_pe) || !aligned16(w_uv))
+      return MLA_ERR_SHAPE;
+  }
+  G = resolve_splits(p);
+  if (G <= 0) return MLA_ERR_UNSUPPORTED;
+  const Layout l = layout_of(p, G);
+  if (!workspace || workspace_bytes < l.total) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_WORKSPACE;
+
+  a.q_nope = q_nope;
+  a.q_pe = q_pe;
+  a.c_kv = c_kv;
+  a.k_pe = k_pe ? k_pe : c_kv;
+  a.kv_scale = kv_scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.c_stride = p.c_kv_stride;
+  a.k_stride = p.k_pe_stride;
+  a.batch = p.batch;
+  a.s_q = p.s_q;
+  a.n_h = p.n_h;
+  a.d_c = p.d_c;
+  a.d_r = p.d_r;
+  a.page_size = p.page_size;
+  a.num_pages = p.num_pages;
+  a.max_pages = p.max_pages_per_seq;
+  a.max_tokens = p.max_pages_per_seq * p.page_size;
+  a.num_splits = G;
+  a.rows_per_group = rows_per_group(p);
+  {
+    const size_t elem = path == Path::kF32 ? 4 : (path == Path::kFp8 ? 1 : 2);
+    a.packed_rows = (k_pe == (const char*)c_kv + (size_t)p.d_c * elem && p.c_kv_stride == p.k_pe_stride) ? 1 : 0;
+  }
+  a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
+  a.split_table = (int32_t*)((char*)workspace + l.table);
+  a.part_lse = (float*)((char*)workspace + l.lse);
+  a.part_u = (char*)workspace + l.u;
+  a.new_c = nullptr;
+  a.new_k = nullptr;
+  a.new_pos = nullptr;
+  a.s_new = 0;
+  return MLA_OK;
+}
+
+mla_status_t launch_fwd(const mla_decode_params_t& p, const mla::AttnParams& a, int G, const void* w_uv, void* out,
+                        float* lse, void* workspace, hipStream_t s) {
+  const Path path = path_of(p);
+  hipError_t e = path == Path::kF32 ? mla::launch_attn_f32(a, s) : mla::launch_attn_mfma(a, path == Path::kFp8, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (!out) return MLA_OK;
+  return combine_impl(p, G, workspace, w_uv, out, lse, s);
+}
+
+mla_status_t prepare_append(const mla_decode_params_t* params, const void* c_new, const void* k_pe_new,
+                            int32_t s_new, mla_dtype_t in_dtype, const int32_t* positions,
+                            const int32_t* block_table, void* c_kv, void* k_pe, float* kv_scale,
+                            mla::AppendParams& a) {
+  if (!params) return MLA_ERR_NULL;
+  const mla_decode_params_t& p = *params;
+  if (p.batch < 1 || s_new < 1 || p.d_c < 1 || p.d_r < 0) return MLA_ERR_SHAPE;
+  if ((long long)p.batch * s_new > INT_MAX) return MLA_ERR_SHAPE;
+  if (p.page_size < 64 || p.page_size % 64 != 0 || p.num_pages < 1 || p.max_pages_per_seq < 1) return MLA_ERR_SHAPE;
+  if (p.c_kv_stride < p.d_c || p.k_pe_stride < p.d_r) return MLA_ERR_SHAPE;
+  if (!c_new || !positions || !block_table || !c_kv) return MLA_ERR_NULL;
+  if (p.d_r > 0 && (!k_pe_new || !k_pe)) return MLA_ERR_NULL;
+  int mode;
+  if (p.kv_dtype == MLA_DTYPE_BF16 && in_dtype == MLA_DTYPE_BF16) mode = 0;
+  else if (p.kv_dtype == MLA_DTYPE_F32 && in_dtype == MLA_DTYPE_F32) mode = 1;
+  else if (p.kv_dtype == MLA_DTYPE_FP8_E4M3 && (in_dtype == MLA_DTYPE_F32 || in_dtype == MLA_DTYPE_BF16)) mode = 2;
+  else return MLA_ERR_DTYPE;
+  if ((mode == 2) != (kv_scale != nullptr)) return mode == 2 ? MLA_ERR_NULL : MLA_ERR_DTYPE;
+  a.c_new = c_new;
+  a.k_new = k_pe_new ? k_pe_new : c_new;
+  a.positions = positions;
+  a.block_table = block_table;
+  a.c_kv = c_kv;
+  a.k_pe = k_pe ? k_pe : c_kv;
+  a.kv_scale = kv_scale;
+  a.c_stride = p.c_kv_stride;
+  a.k_stride = p.k_pe_stride;
+  a.batch = p.batch;
+  a.s_new = s_new;
+  a.d_c = p.d_c;
+  a.d_r = p.d_r;
+  a.page_size = p.page_size;
+  a.num_pages = p.num_pages;
+  a.max_pages = p.max_pages_per_seq;
+  a.in_f32 = in_dtype == MLA_DTYPE_F32;
+  a.mode = mode;
+  return MLA_OK;
+}
+
 }  // namespace
 
 namespace mla {
@@ -192,57 +296,44 @@ mla_status_t mla_decode_fwd(const mla_decode_params_t* params, const void* q_nop
                             const void* c_kv, const void* k_pe, const float* kv_scale,
                             const int32_t* block_table, const int32_t* seq_lens, const void* w_uv, void* out,
                             float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  mla_status_t st = check_common(params);
-  if (st != MLA_OK) return st;
-  const mla_decode_params_t& p = *params;
-  const Path path = path_of(p);
-  if (!q_nope || !q_pe || !c_kv || !block_table || !seq_lens || !w_uv) return MLA_ERR_NULL;
-  if (p.d_r > 0 && !k_pe) return MLA_ERR_NULL;
-  if ((path == Path::kFp8) != (kv_scale != nullptr)) return path == Path::kFp8 ? MLA_ERR_NULL : MLA_ERR_DTYPE;
-  if (path != Path::kF32) {
-    if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(c_kv) || !aligned16(k_pe) || !aligned16(w_uv))
-      return MLA_ERR_SHAPE;
-  }
-  const int G = resolve_splits(p);
-  if (G <= 0) return MLA_ERR_UNSUPPORTED;
-  const Layout l = layout_of(p, G);
-  if (!workspace || workspace_bytes < l.total) return MLA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return MLA_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-
   mla::AttnParams a;
-  a.q_nope = q_nope;
-  a.q_pe = q_pe;
-  a.c_kv = c_kv;
-  a.k_pe = k_pe ? k_pe : c_kv;
-  a.kv_scale = kv_scale;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.c_stride = p.c_kv_stride;
-  a.k_stride = p.k_pe_stride;
-  a.batch = p.batch;
-  a.s_q = p.s_q;
-  a.n_h = p.n_h;
-  a.d_c = p.d_c;
-  a.d_r = p.d_r;
-  a.page_size = p.page_size;
-  a.num_pages = p.num_pages;
-  a.max_pages = p.max_pages_per_seq;
-  a.max_tokens = p.max_pages_per_seq * p.page_size;
-  a.num_splits = G;
-  a.rows_per_group = rows_per_group(p);
-  {
-    const size_t elem = path == Path::kF32 ? 4 : (path == Path::kFp8 ? 1 : 2);
-    a.packed_rows = (k_pe == (const char*)c_kv + (size_t)p.d_c * elem && p.c_kv_stride == p.k_pe_stride) ? 1 : 0;
+  int G = 0;
+  const mla_status_t st = prepare_fwd(params, q_nope, q_pe, c_kv, k_pe, kv_scale, block_table, seq_lens, w_uv,
+                                      workspace, workspace_bytes, a, G);
+  if (st != MLA_OK) return st;
+  return launch_fwd(*params, a, G, w_uv, out, lse, workspace, (hipStream_t)stream);
+}
+
+mla_status_t mla_decode_fwd_append(const mla_decode_params_t* params, const void* c_new, const void* k_pe_new,
+                                   int32_t s_new, mla_dtype_t in_dtype, const int32_t* positions,
+                                   const void* q_nope, const void* q_pe, void* c_kv, void* k_pe, float* kv_scale,
+                                   const int32_t* block_table, const int32_t* seq_lens, const void* w_uv,
+                                   void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  // Everything is validated before anything is launched.
+  mla::AppendParams ap;
+  mla_status_t st = prepare_append(params, c_new, k_pe_new, s_new, in_dtype, positions, block_table, c_kv, k_pe,
+                                   kv_scale, ap);
+  if (st != MLA_OK) return st;
+  mla::AttnParams a;
+  int G = 0;
+  st = prepare_fwd(params, q_nope, q_pe, c_kv, k_pe, kv_scale, block_table, seq_lens, w_uv, workspace,
+                   workspace_bytes, a, G);
+  if (st != MLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const mla_decode_params_t& p = *params;
+  const bool fused = path_of(p) == Path::kBf16 && p.n_h % 128 == 0 && ap.mode == 0 && s_new <= mla::kMaxFusedNew &&
+                     p.d_r > 0 && aligned16(c_new) && aligned16(k_pe_new) && p.c_kv_stride % 8 == 0 &&
+                     p.k_pe_stride % 8 == 0;
+  if (fused) {
+    a.new_c = c_new;
+    a.new_k = k_pe_new;
+    a.new_pos = positions;
+    a.s_new = s_new;
+  } else {
+    st = launch_status(mla::launch_append(ap, s));
+    if (st != MLA_OK) return st;
   }
-  a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
-  a.split_table = (int32_t*)((char*)workspace + l.table);
-  a.part_lse = (float*)((char*)workspace + l.lse);
-  a.part_u = (char*)workspace + l.u;
-  hipError_t e = path == Path::kF32 ? mla::launch_attn_f32(a, s) : mla::launch_attn_mfma(a, path == Path::kFp8, s);
-  if (e != hipSuccess) return MLA_ERR_HIP;
-  if (!out) return MLA_OK;
-  return combine_impl(p, G, workspace, w_uv, out, lse, s);
+  return launch_fwd(p, a, G, w_uv, out, lse, workspace, s);
 }
 
 mla_status_t mla_decode_splitkv_combine(const mla_decode_params_t* params, const void* workspace,
@@ -264,39 +355,10 @@ mla_status_t mla_paged_cache_append(const mla_decode_params_t* params, const voi
                                     int32_t s_new, mla_dtype_t in_dtype, const int32_t* positions,
                                     const int32_t* block_table, void* c_kv, void* k_pe, float* kv_scale,
                                     void* stream) {
-  if (!params) return MLA_ERR_NULL;
-  const mla_decode_params_t& p = *params;
-  if (p.batch < 1 || s_new < 1 || p.d_c < 1 || p.d_r < 0) return MLA_ERR_SHAPE;
-  if ((long long)p.batch * s_new > INT_MAX) return MLA_ERR_SHAPE;
-  if (p.page_size < 64 || p.page_size % 64 != 0 || p.num_pages < 1 || p.max_pages_per_seq < 1) return MLA_ERR_SHAPE;
-  if (p.c_kv_stride < p.d_c || p.k_pe_stride < p.d_r) return MLA_ERR_SHAPE;
-  if (!c_new || !positions || !block_table || !c_kv) return MLA_ERR_NULL;
-  if (p.d_r > 0 && (!k_pe_new || !k_pe)) return MLA_ERR_NULL;
-  int mode;
-  if (p.kv_dtype == MLA_DTYPE_BF16 && in_dtype == MLA_DTYPE_BF16) mode = 0;
-  else if (p.kv_dtype == MLA_DTYPE_F32 && in_dtype == MLA_DTYPE_F32) mode = 1;
-  else if (p.kv_dtype == MLA_DTYPE_FP8_E4M3 && (in_dtype == MLA_DTYPE_F32 || in_dtype == MLA_DTYPE_BF16)) mode = 2;
-  else return MLA_ERR_DTYPE;
-  if ((mode == 2) != (kv_scale != nullptr)) return mode == 2 ? MLA_ERR_NULL : MLA_ERR_DTYPE;
   mla::AppendParams a;
-  a.c_new = c_new;
-  a.k_new = k_pe_new ? k_pe_new : c_new;
-  a.positions = positions;
-  a.block_table = block_table;
-  a.c_kv = c_kv;
-  a.k_pe = k_pe ? k_pe : c_kv;
-  a.kv_scale = kv_scale;
-  a.c_stride = p.c_kv_stride;
-  a.k_stride = p.k_pe_stride;
-  a.batch = p.batch;
-  a.s_new = s_new;
-  a.d_c = p.d_c;
-  a.d_r = p.d_r;
-  a.page_size = p.page_size;
-  a.num_pages = p.num_pages;
-  a.max_pages = p.max_pages_per_seq;
-  a.in_f32 = in_dtype == MLA_DTYPE_F32;
-  a.mode = mode;
+  const mla_status_t st = prepare_append(params, c_new, k_pe_new, s_new, in_dtype, positions, block_table, c_kv,
+                                         k_pe, kv_scale, a);
+  if (st != MLA_OK) return st;
   return launch_status(mla::launch_append(a, (hipStream_t)stream));
 }
 

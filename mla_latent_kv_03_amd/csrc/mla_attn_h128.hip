@@ -85,6 +85,7 @@ struct Smem {
   unsigned char k[kKRing][kKTile];
   unsigned char p[2][kPBuf];                  // [tile % 2][head block][token half][lane] x 16 bytes
   float l[kHeads];                            // row sums, for the column-owning waves
+  unsigned char stash[kMaxFusedNew][kVRow + kKRow];   // fused append: this piece's new rows
   int redo[kWaves];                           // per wave: a tile exceeded the reference maximum
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget of one workgroup");
@@ -198,6 +199,29 @@ void attn_partial_h128(const AttnParams p) {
   pw.init(p.block_table + (size_t)b_guess * p.max_pages, p.max_pages, p.num_pages, 0);
   int pw_b = b_guess;
 
+  // Fused append, pool write of new row `wave` of sequence w (row group 0), at the start:
+  // the wait for its load overlaps the wait for the lengths that the split walk makes
+  // anyway (sequences w + G, w + 2G, .. are written at the end of the launch).  The
+  // stores' completion is never waited for: the tile loop's copy waits only ever count
+  // them as outstanding, which makes those waits stricter, not weaker.
+  if (p.new_c != nullptr && rg == 0 && w < p.batch && wave < p.s_new) {
+    const uint32_t l = lane_id_opaque();
+    const int tok = w * p.s_new + wave;
+    const u32x4 nc = *(const u32x4*)((const char*)p.new_c + (size_t)tok * kDc * 2 + 16 * l);
+    u32x4 nk = u32x4{0u, 0u, 0u, 0u};
+    if (l < kKRow / 16) nk = *(const u32x4*)((const char*)p.new_k + (size_t)tok * kDr * 2 + 16 * l);
+    const int pos = p.new_pos[tok];
+    if (pos >= 0 && pos / p.page_size < p.max_pages) {
+      const int page = p.block_table[(size_t)w * p.max_pages + pos / p.page_size];
+      if (page >= 0 && page < p.num_pages) {
+        const size_t slot = (size_t)page * p.page_size + pos % p.page_size;
+        *(u32x4*)((char*)const_cast<void*>(p.c_kv) + slot * ((size_t)p.c_stride * 2) + 16 * l) = nc;
+        if (l < kKRow / 16)
+          *(u32x4*)((char*)const_cast<void*>(p.k_pe) + slot * ((size_t)p.k_stride * 2) + 16 * l) = nk;
+      }
+    }
+  }
+
   for_each_piece_wave(p.seq_lens, p.batch, p.max_tokens, p.num_splits, w, table, len0, [&](const Piece& pc) {
     const int L = pc.len;
     const int t0 = pc.t0;
@@ -207,6 +231,17 @@ void attn_partial_h128(const AttnParams p) {
     if (pc.b != pw_b) {
       pw.init(p.block_table + (size_t)pc.b * p.max_pages, p.max_pages, p.num_pages, t0 / p.page_size);
       pw_b = pc.b;
+    }
+    // Fused append: the tile (npt) and tile row (nrow) of each new row of this sequence
+    // that lies in the piece's visible tokens, else -1.  Wave-uniform.
+    const bool fused = p.new_c != nullptr;
+    int npt[kMaxFusedNew], nrow[kMaxFusedNew];
+#pragma unroll
+    for (int i = 0; i < kMaxFusedNew; ++i) {
+      const int pos = fused && i < p.s_new ? p.new_pos[(size_t)pc.b * p.s_new + i] : -1;
+      const bool in = pos >= t0 && pos < end;
+      npt[i] = in ? (pos - t0) / kT : -1;
+      nrow[i] = in ? (pos - t0) % kT : -1;
     }
     // Queries of head 32 wave + l32, k-steps of 16: lane holds dims 16 ks + 8 h .. +7.
     bf16x8 qf[kQk];
@@ -312,6 +347,19 @@ void attn_partial_h128(const AttnParams p) {
       // iteration's wait then covers exactly tile 0 and the queries, and the copies do
       // not queue behind 36 query loads.
       uint32_t ready = 0;
+      if (first_pass && fused) {
+        // New row i goes to the stash, copied by wave i (before tile 0's copies, so the
+        // first iteration's wait covers it; the first barrier makes it visible).
+#pragma unroll
+        for (int i = 0; i < kMaxFusedNew; ++i)
+          if (npt[i] >= 0 && wave == i) {
+            const size_t tok = (size_t)pc.b * p.s_new + i;
+            const uint32_t l = lane_id_opaque();
+            buffer_to_lds16(buffer_rsrc((const char*)p.new_c + tok * kDc * 2), 16u * l, 0u, sm.stash[i]);
+            if (l < kKRow / 16)
+              buffer_to_lds16(buffer_rsrc((const char*)p.new_k + tok * kDr * 2), 16u * l, 0u, sm.stash[i] + kVRow);
+          }
+      }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         bool ok;
@@ -326,6 +374,30 @@ void attn_partial_h128(const AttnParams p) {
         wait_vmcnt<kCopies>();     // this wave's copies of tile `it` have landed, it+1's in flight
         lds_barrier();             // tile `it` and every wave's probabilities of it-1 are in LDS
         const bool cur = (ready & 1u) != 0;       // tile `it` is scored
+        if (fused && cur && (npt[0] == it || npt[1] == it)) {
+          // Fused append: rows of this tile whose source is a new row (its own row, and the
+          // rows past the last visible one when it is the last) take the stashed row; each
+          // wave patches its own rows, then a second barrier publishes them.
+          const int tt = t0 + it * kT;
+          const int last = min(tt + kT, end) - 1 - tt;
+          const uint32_t l = lane_id_opaque();
+#pragma unroll
+          for (int i = 0; i < kMaxFusedNew; ++i) {
+            if (npt[i] != it) continue;
+#pragma unroll 1
+            for (int j = 0; j < 8; ++j) {
+              const int rr = 8 * wave + j;
+              if (min(rr, last) != nrow[i]) continue;
+              const u32x4 v = *(const u32x4*)(sm.stash[i] + 16 * l);
+              *(u32x4*)(sm.v[vs] + rr * kVRow + 16 * (l ^ (uint32_t)swz_v(rr))) = v;
+              if (l < kKRow / 16) {
+                const u32x4 k = *(const u32x4*)(sm.stash[i] + kVRow + 16 * l);
+                *(u32x4*)(sm.k[ks3] + rr * kKRow + 16 * (l ^ (uint32_t)swz_k(rr))) = k;
+              }
+            }
+          }
+          lds_barrier();
+        }
         bool next_ok;
         // Tile it+2 goes to ring slots last read in iteration it-1, which every wave
         // has finished (barrier above).
@@ -496,10 +568,34 @@ void attn_partial_h128(const AttnParams p) {
           *(bf16x4*)(up + 32 * cl + 8 * g4) = to_bf16x4(o);
         }
     }
-    // The next piece's prologue refills ring slots 0 and 1 and the row sums, which other
-    // waves may still be reading for this piece.
+    // The next piece's prologue refills ring slots 0 and 1, the row sums and the stash,
+    // which other waves may still be reading for this piece.
     __syncthreads();
   });
+
+  // Fused append: the rest of this share's pool writes (sequences w + G, w + 2G, ..).  No
+  // tile of this launch reads these rows from the pool.
+  if (p.new_c && rg == 0) {
+    const uint32_t l = lane_id_opaque();
+    const size_t c_row_b = (size_t)p.c_stride * 2, k_row_b = (size_t)p.k_stride * 2;
+    for (int b = w + p.num_splits; b < p.batch; b += p.num_splits)
+      for (int i = wave; i < p.s_new; i += kWaves) {
+        const int tok = b * p.s_new + i;
+        const int pos = p.new_pos[tok];
+        if (pos < 0) continue;
+        const int pidx = pos / p.page_size;
+        if (pidx >= p.max_pages) continue;
+        const int page = p.block_table[(size_t)b * p.max_pages + pidx];
+        if (page < 0 || page >= p.num_pages) continue;
+        const size_t slot = (size_t)page * p.page_size + pos % p.page_size;
+        const u32x4 c = *(const u32x4*)((const char*)p.new_c + (size_t)tok * kDc * 2 + 16 * l);
+        *(u32x4*)((char*)const_cast<void*>(p.c_kv) + slot * c_row_b + 16 * l) = c;
+        if (l < kKRow / 16) {
+          const u32x4 k = *(const u32x4*)((const char*)p.new_k + (size_t)tok * kDr * 2 + 16 * l);
+          *(u32x4*)((char*)const_cast<void*>(p.k_pe) + slot * k_row_b + 16 * l) = k;
+        }
+      }
+  }
 }
 
 }  // namespace

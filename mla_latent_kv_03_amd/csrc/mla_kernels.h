@@ -26,7 +26,16 @@ struct AttnParams {
   int32_t* split_table;      // [B][2]
   float* part_lse;           // [G + B][s_q][n_h]
   void* part_u;              // [G + B][s_q][n_h][d_c]: bf16 (bf16 / E4M3 caches) or float32 (fp32 path)
+  // Fused append (128-head bf16 kernel only; new_c == null otherwise): the new rows
+  // [B][s_new][d_c] / [B][s_new][d_r] (bf16) at positions [B][s_new] are written to the
+  // pool by the workgroups of row group 0 (sequence b by share b % G) at the end of the
+  // launch, and every tile that holds a new position gets that row from new_c / new_k.
+  const void* new_c;
+  const void* new_k;
+  const int32_t* new_pos;
+  int32_t s_new;             // 1 .. kMaxFusedNew
 };
+constexpr int kMaxFusedNew = 2;
 
 // Arguments of the combine + up-projection kernels.
 struct CombineParams {
