@@ -168,7 +168,7 @@ void attn_partial_h128(const AttnParams p) {
   //    (rows 4h + r (+ 8 e) have sv = 4r + h + 2e);
   //  - probability buffer: 16 bytes per lane.
   struct LaneOffsets {
-    uint32_t qk_v, qk_k, tr, pb;
+    uint32_t ln, qk_v, qk_k, tr, pb;
   };
   auto lane_offsets = [&]() {
     const uint32_t ln = lane_id_opaque();
@@ -176,6 +176,7 @@ void attn_partial_h128(const AttnParams p) {
     const int tr_i = l & 15, tr_r = tr_i >> 2, tr_q = tr_i & 3, tr_b1 = (l >> 4) & 1;
     const int tr_lc = (2 * tr_b1 + (tr_q >> 1)) ^ (4 * tr_r + hh);
     LaneOffsets o;
+    o.ln = ln;
     o.qk_v = (uint32_t)(lr * kVRow + 16 * (hh ^ swz_v(lr)));                   // ^ 32 (ks % 8), + 256 (ks / 8)
     o.qk_k = (uint32_t)(kVRing * kVTile + lr * kKRow + 16 * (hh ^ swz_k(lr)));  // ^ 32 (ks - 32)
     o.tr = (uint32_t)((4 * hh + tr_r) * kVRow + 16 * tr_lc + 8 * (tr_q & 1) + 256 * wave);
@@ -302,8 +303,7 @@ void attn_partial_h128(const AttnParams p) {
     // Copy j of this wave's 9 for tile tc: latent row 8 wave + j (j < 8; lane l: stored
     // chunk l) or the RoPE block (j = 8; lane l: row 8 wave + l/8, stored chunk l%8).
     // Per-lane offsets are recomputed from the lane index rather than kept live.
-    auto copy_row = [&](const TileCopy& tc, int j) {
-      const uint32_t lz = lane_id_opaque();
+    auto copy_row = [&](const TileCopy& tc, int j, uint32_t lz) {
       if (j < 8) {
         const int r = 8 * wave + j;
         buffer_to_lds16(tc.vres, 16u * (lz ^ (uint32_t)swz_v(r)), (uint32_t)min(r, tc.last) * c_row,
@@ -347,6 +347,7 @@ void attn_partial_h128(const AttnParams p) {
       // iteration's wait then covers exactly tile 0 and the queries, and the copies do
       // not queue behind 36 query loads.
       uint32_t ready = 0;
+      const uint32_t lz0 = lane_id_opaque();
       if (first_pass && fused) {
         // New row i goes to the stash, copied by wave i (before tile 0's copies, so the
         // first iteration's wait covers it; the first barrier makes it visible).
@@ -366,7 +367,7 @@ void attn_partial_h128(const AttnParams p) {
         const TileCopy tc = prepare_next(t < ntiles, ok);
         ready |= ok ? (1u << t) : 0u;
 #pragma unroll
-        for (int j = 0; j < kCopies; ++j) copy_row(tc, j);
+        for (int j = 0; j < kCopies; ++j) copy_row(tc, j, lz0);
         if (t == 0 && first_pass) load_queries();
       }
       int vs = 0, ks3 = 0;   // ring slots of tile `it`
@@ -398,12 +399,6 @@ void attn_partial_h128(const AttnParams p) {
           }
           lds_barrier();
         }
-        bool next_ok;
-        // Tile it+2 goes to ring slots last read in iteration it-1, which every wave
-        // has finished (barrier above).
-        const TileCopy tn = prepare_next(it + 2 < ntiles, next_ok);
-        ready |= next_ok ? 4u : 0u;
-
         // Per-lane LDS offsets of this iteration: ring slot + fixed lane part; the XOR
         // swizzles only touch bits 4..7, below the slot bits.
         const unsigned char* lds = (const unsigned char*)&sm;
@@ -439,6 +434,13 @@ void attn_partial_h128(const AttnParams p) {
         va[0] = vfrag(0, 0);
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) pb[0][hb] = pfrag(hb, 0);
+        // The copy bookkeeping of tile it+2 (scalar work) runs while those first reads are
+        // in flight.  Tile it+2 goes to ring slots last read in iteration it-1, which every
+        // wave has finished (barrier above).
+        __builtin_amdgcn_sched_barrier(0);
+        bool next_ok;
+        const TileCopy tn = prepare_next(it + 2 < ntiles, next_ok);
+        ready |= next_ok ? 4u : 0u;
 #pragma unroll
         for (int ks = 0; ks < kQk; ++ks) {
           __builtin_amdgcn_sched_barrier(0);   // keep the source order: reads ahead of use
@@ -453,7 +455,7 @@ void attn_partial_h128(const AttnParams p) {
           if (ks == 28) va[2] = vfrag(2, 1);
           if (ks >= 30 && ks < 34) pb[1][ks - 30] = pfrag(ks - 30, 1);
           if (ks == 35) va[3] = vfrag(3, 1);
-          if (ks % 4 == 1) copy_row(tn, ks / 4);                                    // ks = 1, 5, .., 33
+          if (ks % 4 == 1) copy_row(tn, ks / 4, lo.ln);                             // ks = 1, 5, .., 33
           if (ks == 0)
             score_mfma_first(s, kq[ks % (kKPf + 1)], qf[ks]);
           else
