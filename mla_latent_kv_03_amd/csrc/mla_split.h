@@ -261,14 +261,25 @@ struct PageWindow {
     num_pages = num_pages_;
     load(first_page);
   }
+  // Waits for a reload right where it is issued.  Without it the compiler, which cannot
+  // tell whether the load on the rare path ran, waits at every later lookup, and that
+  // wait (for all of the wave's outstanding vector-memory operations) would also wait
+  // for the tile copies in flight.
+  __device__ void settle() { asm volatile("v_mov_b32 %0, %0" : "+v"(ids)); }
   // Make `page_idx` (at or before the next lookups) readable: reloads the window if it
   // starts after page_idx, e.g. when a second pass over a piece goes back to its start.
   __device__ void rewind(int page_idx) {
-    if (page_idx < base) load(page_idx);
+    if (page_idx < base) {
+      load(page_idx);
+      settle();
+    }
   }
   // page id of logical page `page_idx` (wave-uniform), -1 if invalid
   __device__ int get(int page_idx) {
-    if (page_idx >= base + 64) load(page_idx - 32 > base ? page_idx - 32 : base + 32);
+    if (page_idx >= base + 64) {
+      load(page_idx - 32 > base ? page_idx - 32 : base + 32);
+      settle();
+    }
     const int id = __builtin_amdgcn_readlane(ids, page_idx - base);
     return id >= 0 && id < num_pages ? id : -1;
   }
