@@ -151,7 +151,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 
 void attn_partial_h128(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
 
-  const int w = blockIdx.x;
+  // Consecutive shares (the pieces of one sequence) on one XCD: workgroups are dispatched
+  // to the 8 XCDs round-robin, so workgroup i takes share (i % 8) * (G / 8) + i / 8.
+  const int w = p.num_splits % 8 == 0 ? (int)(blockIdx.x % 8) * (p.num_splits / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   const int rg = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
