@@ -1,5 +1,5 @@
-// Partial attention of absorbed MLA decode on gfx950, bf16 latent cache, 128 heads
-// of one query position per workgroup.
+// Partial attention of absorbed MLA decode on gfx950, bf16 or E4M3 latent cache, 128
+// heads of one query position per workgroup.
 //
 // For every piece of the split rule and every head i of the workgroup:
 //   s_j = softmax_scale * (q_nope_i . c_j + q_pe_i . k_pe_j)       (page "MLA deep compression":
@@ -48,6 +48,14 @@
 // first visible tile and the accumulators are never rescaled.  If a later tile exceeds
 // m by more than 64 (log2 units), the workgroup recomputes the piece with m = the exact
 // maximum, which the first pass has seen by then.
+//
+// E4M3 caches (page "MLA deep compression" gives the cache bytes per token as the lever;
+// one fp32 scale per token, value = code * scale): the same pipeline on tiles of 512 +
+// 64 bytes per token plus the scales, at half the copies.  A 128-bit score read gives 16
+// values, the operands of two MFMA k-steps (the queries are loaded in the same k order);
+// a transposed 8-bit read gives a whole 8-token value operand.  Both are widened to bf16
+// exactly; the token scales multiply the scores and the probabilities (rounded to bf16
+// afterwards), which is the dequantized attention.
 
 #include "mla_device.h"
 #include "mla_kernels.h"
@@ -72,7 +80,19 @@ constexpr int kKRing = 3;
 constexpr int kQk = (kDc + kDr) / 16;         // 36 score k-steps of 16
 constexpr int kQkV = kDc / 16;                // the first 32 read latent rows; the last 4 the RoPE part
 constexpr int kPv = 32;                       // accumulation MFMAs per tile: 2 token halves x 4 x 4 blocks
-constexpr int kCopies = 9;                    // per wave and tile: 8 latent rows + 1 RoPE block
+// Per element type of the cache: bf16 rows (1024 + 128 bytes) or E4M3 rows (512 + 64
+// bytes, plus one fp32 scale per token).  kCopies: 1 KiB copies per wave and tile (bf16:
+// 8 latent rows + 1 RoPE block; E4M3: 4 two-row latent blocks + a RoPE block or the
+// scales, none for wave 3).
+template <bool FP8>
+struct Layout {
+  static constexpr int kVRow = FP8 ? kDc : kDc * 2;
+  static constexpr int kVTile = kT * kVRow;
+  static constexpr int kKRow = FP8 ? kDr : kDr * 2;
+  static constexpr int kKTile = kT * kKRow;
+  static constexpr int kCopies = FP8 ? 5 : 9;
+};
+constexpr int kCopies = 9;
 constexpr int kPBuf = kT * kHeads * 2;        // 8 KiB of bf16 probabilities per tile
 #ifndef MLA_H128_KPF
 #define MLA_H128_KPF 2
@@ -80,15 +100,17 @@ constexpr int kPBuf = kT * kHeads * 2;        // 8 KiB of bf16 probabilities per
 constexpr int kKPf = MLA_H128_KPF;            // score operands are read this many k-steps ahead
 constexpr float kHeadroom = 64.f;             // tolerated excess over the reference maximum (log2 units)
 
+template <bool FP8>
 struct Smem {
-  unsigned char v[kVRing][kVTile];
-  unsigned char k[kKRing][kKTile];
+  unsigned char v[kVRing][Layout<FP8>::kVTile];
+  unsigned char k[kKRing][Layout<FP8>::kKTile];
   unsigned char p[2][kPBuf];                  // [tile % 2][head block][token half][lane] x 16 bytes
+  float sc[FP8 ? kKRing : 1][64];             // E4M3: per-token scales of the tile (32 used)
   float l[kHeads];                            // row sums, for the column-owning waves
   unsigned char stash[kMaxFusedNew][kVRow + kKRow];   // fused append: this piece's new rows
   int redo[kWaves];                           // per wave: a tile exceeded the reference maximum
 };
-static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget of one workgroup");
+static_assert(sizeof(Smem<false>) <= 160 * 1024 && sizeof(Smem<true>) <= 160 * 1024, "LDS budget of one workgroup");
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   // C[32x32] += A[32x16] B[16x32]: lane l holds A[l%32][8(l/32) + j], B[8(l/32) + j][l%32]
@@ -134,6 +156,23 @@ __device__ __forceinline__ uint32_t opaque_zero() {
 
 __device__ __forceinline__ int swz_v(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
+// E4M3 rows: 16-byte chunk c (of 32) of latent row r is stored at c ^ swz_v8(r), a
+// permutation of r's low 4 bits (bit 0 <- r bit 2, bits 1-2 <- r bits 0-1, bit 3 <- r
+// bit 3): 16 consecutive rows get 16 positions (score reads), and the 8 rows that one
+// 16-lane block of a transposed read covers (4h + 0..3 and 8 + 4h + 0..3) get 8 even or
+// 8 odd ones, so two adjacent chunks of them fill all 16 positions.  RoPE rows (4 chunks)
+// use c ^ ((r / 4) % 4).
+__device__ __forceinline__ int swz_v8(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+__device__ __forceinline__ int swz_k8(int r) { return (r >> 2) & 3; }
+
+// 8 E4M3 values (two dwords, byte j = value j) to bf16, exactly.  (The conversion's own
+// scale operand is not used for the per-token scales: MX-style conversions scale by a
+// power of two.)
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = e4m3x2_to_bf16<false>(w0), b = e4m3x2_to_bf16<true>(w0);
+  const bf16x2 c = e4m3x2_to_bf16<false>(w1), d = e4m3x2_to_bf16<true>(w1);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left alone
@@ -147,9 +186,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_partial_h128(const AttnParams p) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
+  __shared__ __attribute__((aligned(16))) Smem<FP8> sm;
+  using LT = Layout<FP8>;
 
   // Consecutive shares (the pieces of one sequence) on one XCD: workgroups are dispatched
   // to the 8 XCDs round-robin, so workgroup i takes share (i % 8) * (G / 8) + i / 8.
@@ -169,20 +210,34 @@ void attn_partial_h128(const AttnParams p) {
   //    of a 32-column block, lane 4r + q of the block the 4 columns 4q.. of token row r
   //    (rows 4h + r (+ 8 e) have sv = 4r + h + 2e);
   //  - probability buffer: 16 bytes per lane.
+  //  E4M3 tiles (16-byte chunks of 16 values):
+  //  - score reads: token l32, the 16 values of chunk 2 kp + h (k-steps 2 kp and 2 kp + 1
+  //    take bytes 0..7 and 8..15), stored at (2 kp + h) ^ swz_v8(l32);
+  //  - transposed latent reads (8-bit): 16-lane block b = lane/16, lane 2r + q of the
+  //    block: token row 8 (r/4) + 4 (b/2) + r%4, bytes 8q.. of chunk 8 wave + 2 cl + b%2.
   struct LaneOffsets {
     uint32_t ln, qk_v, qk_k, tr, pb;
   };
   auto lane_offsets = [&]() {
     const uint32_t ln = lane_id_opaque();
     const int l = (int)ln, lr = l & 31, hh = l >> 5;
-    const int tr_i = l & 15, tr_r = tr_i >> 2, tr_q = tr_i & 3, tr_b1 = (l >> 4) & 1;
-    const int tr_lc = (2 * tr_b1 + (tr_q >> 1)) ^ (4 * tr_r + hh);
     LaneOffsets o;
     o.ln = ln;
-    o.qk_v = (uint32_t)(lr * kVRow + 16 * (hh ^ swz_v(lr)));                   // ^ 32 (ks % 8), + 256 (ks / 8)
-    o.qk_k = (uint32_t)(kVRing * kVTile + lr * kKRow + 16 * (hh ^ swz_k(lr)));  // ^ 32 (ks - 32)
-    o.tr = (uint32_t)((4 * hh + tr_r) * kVRow + 16 * tr_lc + 8 * (tr_q & 1) + 256 * wave);
-    o.pb = (uint32_t)(kVRing * kVTile + kKRing * kKTile) + 16 * ln;
+    o.pb = (uint32_t)offsetof(Smem<FP8>, p) + 16 * ln;
+    if constexpr (!FP8) {
+      const int tr_i = l & 15, tr_r = tr_i >> 2, tr_q = tr_i & 3, tr_b1 = (l >> 4) & 1;
+      const int tr_lc = (2 * tr_b1 + (tr_q >> 1)) ^ (4 * tr_r + hh);
+      o.qk_v = (uint32_t)(lr * kVRow + 16 * (hh ^ swz_v(lr)));                   // ^ 32 (ks % 8), + 256 (ks / 8)
+      o.qk_k = (uint32_t)(kVRing * kVTile + lr * kKRow + 16 * (hh ^ swz_k(lr)));  // ^ 32 (ks - 32)
+      o.tr = (uint32_t)((4 * hh + tr_r) * kVRow + 16 * tr_lc + 8 * (tr_q & 1) + 256 * wave);
+    } else {
+      const int b = l >> 4, r = (l & 15) >> 1, q = l & 1;
+      const int tok = 8 * (r >> 2) + 4 * (b >> 1) + (r & 3);
+      const int c0 = 8 * wave + (b & 1);
+      o.qk_v = (uint32_t)(lr * LT::kVRow + 16 * (hh ^ swz_v8(lr)));                                 // ^ 32 kp
+      o.qk_k = (uint32_t)(offsetof(Smem<FP8>, k) + lr * LT::kKRow + 16 * (hh ^ swz_k8(lr)));        // ^ 32 (kp - 16)
+      o.tr = (uint32_t)(tok * LT::kVRow + 16 * (c0 ^ swz_v8(tok)) + 8 * q);                           // ^ 32 cl, + 8192 th
+    }
     return o;
   };
 
@@ -190,7 +245,7 @@ void attn_partial_h128(const AttnParams p) {
   // Ring slot 3 starts zeroed: the accumulation step that runs before a pass's first
   // tile reads it with zero probabilities, and 0 * (stale bits) must not produce NaN.
   // Afterwards the ring only ever holds cache rows or zeros.
-  for (int i = threadIdx.x; i < kVTile / 16; i += 64 * kWaves)
+  for (int i = threadIdx.x; i < LT::kVTile / 16; i += 64 * kWaves)
     ((u32x4*)sm.v[kVRing - 1])[i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();   // before any wave's first tile copies land in the ring
 
@@ -246,20 +301,31 @@ void attn_partial_h128(const AttnParams p) {
       npt[i] = in ? (pos - t0) / kT : -1;
       nrow[i] = in ? (pos - t0) % kT : -1;
     }
-    // Queries of head 32 wave + l32, k-steps of 16: lane holds dims 16 ks + 8 h .. +7.
+    // Queries of head 32 wave + l32, k-steps of 16: lane holds dims 16 ks + 8 h .. +7
+    // (E4M3: k-step 2 kp + s holds dims 32 kp + 16 h + 8 s .. +7, the order of the score
+    // reads; a contraction may take its k index in any order both operands share).
     bf16x8 qf[kQk];
     auto load_queries = [&]() {
       const int ql = (int)lane_id_opaque(), l32 = ql & 31, h = ql >> 5;
       const size_t qrow = ((size_t)pc.b * p.s_q + q_pos) * p.n_h + head_base + 32 * wave + l32;
-      const bf16* qn = (const bf16*)p.q_nope + qrow * kDc + 8 * h;
-      const bf16* qp = (const bf16*)p.q_pe + qrow * kDr + 8 * h;
+      if constexpr (!FP8) {
+        const bf16* qn = (const bf16*)p.q_nope + qrow * kDc + 8 * h;
+        const bf16* qp = (const bf16*)p.q_pe + qrow * kDr + 8 * h;
 #pragma unroll
-      for (int ks = 0; ks < kQkV; ++ks) qf[ks] = *(const bf16x8*)(qn + 16 * ks);
+        for (int ks = 0; ks < kQkV; ++ks) qf[ks] = *(const bf16x8*)(qn + 16 * ks);
 #pragma unroll
-      for (int kk = 0; kk < kQk - kQkV; ++kk) qf[kQkV + kk] = *(const bf16x8*)(qp + 16 * kk);
+        for (int kk = 0; kk < kQk - kQkV; ++kk) qf[kQkV + kk] = *(const bf16x8*)(qp + 16 * kk);
+      } else {
+        const bf16* qn = (const bf16*)p.q_nope + qrow * kDc + 16 * h;
+        const bf16* qp = (const bf16*)p.q_pe + qrow * kDr + 16 * h;
+#pragma unroll
+        for (int ks = 0; ks < kQkV; ++ks) qf[ks] = *(const bf16x8*)(qn + 32 * (ks >> 1) + 8 * (ks & 1));
+#pragma unroll
+        for (int kk = 0; kk < kQk - kQkV; ++kk) qf[kQkV + kk] = *(const bf16x8*)(qp + 32 * (kk >> 1) + 8 * (kk & 1));
+      }
     };
     const int tiles_per_page = p.page_size / kT;
-    const uint32_t c_row = (uint32_t)p.c_stride * 2u, k_row = (uint32_t)p.k_stride * 2u;
+    const uint32_t c_row = (uint32_t)p.c_stride * (FP8 ? 1u : 2u), k_row = (uint32_t)p.k_stride * (FP8 ? 1u : 2u);
 
     // Copy cursor: the next tile to enqueue, its logical page, its tile index within
     // that page and its ring slots.
@@ -278,7 +344,7 @@ void attn_partial_h128(const AttnParams p) {
     // invalid page, or past the piece, gets zero-length resources: its copies read
     // nothing and fill their ring slots with zeros.
     struct TileCopy {
-      __amdgpu_buffer_rsrc_t vres, kres;
+      __amdgpu_buffer_rsrc_t vres, kres, sres;
       int last, vs, ks;
     };
     // Describe the cursor's tile and advance the cursor (scalar work only); `ok` tells
@@ -290,6 +356,7 @@ void attn_partial_h128(const AttnParams p) {
       const long long slot0 = ok ? (long long)page * p.page_size + i_tip * kT : 0;
       tc.vres = buffer_rsrc((const char*)p.c_kv + slot0 * c_row, ok ? 0x7fffffff : 0);
       tc.kres = buffer_rsrc((const char*)p.k_pe + slot0 * k_row, ok ? 0x7fffffff : 0);
+      if constexpr (FP8) tc.sres = buffer_rsrc(p.kv_scale + slot0, ok ? 0x7fffffff : 0);
       tc.last = min(i_tt + kT, end) - 1 - i_tt;   // rows past `last` re-read it
       tc.vs = i_vs;
       tc.ks = i_ks;
@@ -305,16 +372,46 @@ void attn_partial_h128(const AttnParams p) {
     // Copy j of this wave's 9 for tile tc: latent row 8 wave + j (j < 8; lane l: stored
     // chunk l) or the RoPE block (j = 8; lane l: row 8 wave + l/8, stored chunk l%8).
     // Per-lane offsets are recomputed from the lane index rather than kept live.
+    // E4M3, copy j of this wave's 5: latent rows 2i, 2i + 1 with i = wave + 4j (j < 4;
+    // lane l: row 2i + l/32, stored chunk l%32), then for waves 0 and 1 the RoPE rows
+    // 16 wave .. + 15 (lane l: row 16 wave + l/4, stored chunk l%4) and for wave 2 the
+    // scales (lane l: token min(l, last), 4 bytes).
     auto copy_row = [&](const TileCopy& tc, int j, uint32_t lz) {
-      if (j < 8) {
-        const int r = 8 * wave + j;
-        buffer_to_lds16(tc.vres, 16u * (lz ^ (uint32_t)swz_v(r)), (uint32_t)min(r, tc.last) * c_row,
-                        sm.v[tc.vs] + r * kVRow);
+      if constexpr (!FP8) {
+        if (j < 8) {
+          const int r = 8 * wave + j;
+          buffer_to_lds16(tc.vres, 16u * (lz ^ (uint32_t)swz_v(r)), (uint32_t)min(r, tc.last) * c_row,
+                          sm.v[tc.vs] + r * kVRow);
+        } else {
+          const int krow = 8 * wave + (int)(lz >> 3);
+          const uint32_t kchunk = (lz & 7u) ^ (uint32_t)swz_k(krow);
+          const uint32_t koff = (uint32_t)min(krow, tc.last) * k_row + 16u * kchunk;
+          buffer_to_lds16(tc.kres, koff, 0u, sm.k[tc.ks] + wave * 1024);
+        }
       } else {
-        const int krow = 8 * wave + (int)(lz >> 3);
-        const uint32_t kchunk = (lz & 7u) ^ (uint32_t)swz_k(krow);
-        const uint32_t koff = (uint32_t)min(krow, tc.last) * k_row + 16u * kchunk;
-        buffer_to_lds16(tc.kres, koff, 0u, sm.k[tc.ks] + wave * 1024);
+        if (j < 4) {
+          const int i = wave + 4 * j;
+          const int r = 2 * i + (int)(lz >> 5);
+          const uint32_t chunk = (lz & 31u) ^ (uint32_t)swz_v8(r);
+          buffer_to_lds16(tc.vres, (uint32_t)min(r, tc.last) * c_row + 16u * chunk, 0u, sm.v[tc.vs] + i * 1024);
+        } else if (wave < 2) {
+          const int krow = 16 * wave + (int)(lz >> 2);
+          const uint32_t kchunk = (lz & 3u) ^ (uint32_t)swz_k8(krow);
+          buffer_to_lds16(tc.kres, (uint32_t)min(krow, tc.last) * k_row + 16u * kchunk, 0u, sm.k[tc.ks] + wave * 1024);
+        } else if (wave == 2) {
+          buffer_to_lds4(tc.sres, 4u * (uint32_t)min((int)lz, tc.last), 0u, sm.sc[tc.ks]);
+        }
+      }
+    };
+    // This wave's copies of all but the most recently enqueued tile have landed.
+    auto wait_copies = [&]() {
+      if constexpr (!FP8) {
+        wait_vmcnt<kCopies>();
+      } else {
+        if (wave == 3)
+          wait_vmcnt<4>();
+        else
+          wait_vmcnt<5>();
       }
     };
 
@@ -369,15 +466,15 @@ void attn_partial_h128(const AttnParams p) {
         const TileCopy tc = prepare_next(t < ntiles, ok);
         ready |= ok ? (1u << t) : 0u;
 #pragma unroll
-        for (int j = 0; j < kCopies; ++j) copy_row(tc, j, lz0);
+        for (int j = 0; j < LT::kCopies; ++j) copy_row(tc, j, lz0);
         if (t == 0 && first_pass) load_queries();
       }
       int vs = 0, ks3 = 0;   // ring slots of tile `it`
       for (int it = 0; it <= ntiles; ++it) {
-        wait_vmcnt<kCopies>();     // this wave's copies of tile `it` have landed, it+1's in flight
+        wait_copies();             // this wave's copies of tile `it` have landed, it+1's in flight
         lds_barrier();             // tile `it` and every wave's probabilities of it-1 are in LDS
         const bool cur = (ready & 1u) != 0;       // tile `it` is scored
-        if (fused && cur && (npt[0] == it || npt[1] == it)) {
+        if (!FP8 && fused && cur && (npt[0] == it || npt[1] == it)) {
           // Fused append: rows of this tile whose source is a new row (its own row, and the
           // rows past the last visible one when it is the last) take the stashed row; each
           // wave patches its own rows, then a second barrier publishes them.
@@ -392,10 +489,10 @@ void attn_partial_h128(const AttnParams p) {
               const int rr = 8 * wave + j;
               if (min(rr, last) != nrow[i]) continue;
               const u32x4 v = *(const u32x4*)(sm.stash[i] + 16 * l);
-              *(u32x4*)(sm.v[vs] + rr * kVRow + 16 * (l ^ (uint32_t)swz_v(rr))) = v;
+              *(u32x4*)(sm.v[vs] + rr * LT::kVRow + 16 * (l ^ (uint32_t)swz_v(rr))) = v;
               if (l < kKRow / 16) {
                 const u32x4 k = *(const u32x4*)(sm.stash[i] + kVRow + 16 * l);
-                *(u32x4*)(sm.k[ks3] + rr * kKRow + 16 * (l ^ (uint32_t)swz_k(rr))) = k;
+                *(u32x4*)(sm.k[ks3] + rr * LT::kKRow + 16 * (l ^ (uint32_t)swz_k(rr))) = k;
               }
             }
           }
@@ -405,21 +502,32 @@ void attn_partial_h128(const AttnParams p) {
         // swizzles only touch bits 4..7, below the slot bits.
         const unsigned char* lds = (const unsigned char*)&sm;
         const LaneOffsets lo = lane_offsets();
-        const uint32_t bq = (uint32_t)(vs * kVTile) + lo.qk_v;
-        const uint32_t bk = (uint32_t)(ks3 * kKTile) + lo.qk_k;
-        const uint32_t bt = (uint32_t)(((vs + kVRing - 1) & (kVRing - 1)) * kVTile) + lo.tr;
+        const uint32_t bq = (uint32_t)(vs * LT::kVTile) + lo.qk_v;
+        const uint32_t bk = (uint32_t)(ks3 * LT::kKTile) + lo.qk_k;
+        const uint32_t bt = (uint32_t)(((vs + kVRing - 1) & (kVRing - 1)) * LT::kVTile) + lo.tr;
         const uint32_t bp = (uint32_t)(((it + 1) & 1) * kPBuf) + lo.pb;
         auto kfrag = [&](int ks) -> bf16x8 {
           if (ks < kQkV) return *(const bf16x8*)(lds + ((bq ^ (32u * (ks & 7))) + 256 * (ks >> 3)));
           return *(const bf16x8*)(lds + (bk ^ (32u * (ks - kQkV))));
         };
+        // E4M3: the 16 values of score k-steps 2 kp and 2 kp + 1.
+        auto kraw = [&](int kp) -> u32x4 {
+          if (kp < kQkV / 2) return *(const u32x4*)(lds + (bq ^ (32u * kp)));
+          return *(const u32x4*)(lds + (bk ^ (32u * (kp - kQkV / 2))));
+        };
         // V^T fragment of this wave's column block cl (32 columns) and token half th of
         // tile it-1.
         auto vfrag = [&](int cl, int th) -> bf16x8 {
-          const uint32_t o = 16384 * th;
-          const bf16x4 lo = lds_read_tr16(lds + ((bt ^ (64u * cl)) + o));
-          const bf16x4 hi = lds_read_tr16(lds + ((bt ^ (64u * cl ^ 32u)) + o + 8192));
-          return concat4(lo, hi);
+          if constexpr (!FP8) {
+            const uint32_t o = 16384 * th;
+            const bf16x4 lo = lds_read_tr16(lds + ((bt ^ (64u * cl)) + o));
+            const bf16x4 hi = lds_read_tr16(lds + ((bt ^ (64u * cl ^ 32u)) + o + 8192));
+            return concat4(lo, hi);
+          } else {
+            const uint32_t o = 16 * LT::kVRow * th;
+            const u32x2 w8 = lds_read_tr8(lds + ((bt ^ (32u * cl)) + o));
+            return e4m3x8_to_bf16(w8[0], w8[1]);
+          }
         };
         // P^T fragment of head block hb and token half th of tile it-1.
         auto pfrag = [&](int hb, int th) -> bf16x8 { return *(const bf16x8*)(lds + bp + (hb * 2 + th) * 1024); };
@@ -431,8 +539,14 @@ void attn_partial_h128(const AttnParams p) {
         // one wave per SIMD the reads' latency has to hide behind this wave's own MFMAs.
         f32x16 s;
         bf16x8 kq[kKPf + 1], va[4], pb[2][4];
+        u32x4 kr[2];          // E4M3: raw score operands, one k-step pair ahead
+        bf16x8 kop[2];        // E4M3: the current pair, widened exactly
+        if constexpr (!FP8) {
 #pragma unroll
-        for (int j = 0; j < kKPf; ++j) kq[j] = kfrag(j);
+          for (int j = 0; j < kKPf; ++j) kq[j] = kfrag(j);
+        } else {
+          kr[0] = kraw(0);
+        }
         va[0] = vfrag(0, 0);
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) pb[0][hb] = pfrag(hb, 0);
@@ -446,7 +560,14 @@ void attn_partial_h128(const AttnParams p) {
 #pragma unroll
         for (int ks = 0; ks < kQk; ++ks) {
           __builtin_amdgcn_sched_barrier(0);   // keep the source order: reads ahead of use
-          if (ks + kKPf < kQk) kq[(ks + kKPf) % (kKPf + 1)] = kfrag(ks + kKPf);
+          if constexpr (!FP8) {
+            if (ks + kKPf < kQk) kq[(ks + kKPf) % (kKPf + 1)] = kfrag(ks + kKPf);
+          } else if (ks % 2 == 0) {
+            if (ks / 2 + 1 < kQk / 2) kr[(ks / 2 + 1) % 2] = kraw(ks / 2 + 1);
+            const u32x4 r = kr[(ks / 2) % 2];
+            kop[0] = e4m3x8_to_bf16(r[0], r[1]);
+            kop[1] = e4m3x8_to_bf16(r[2], r[3]);
+          }
           // Step a runs at ks = 2a + 3.  va[cl] holds token half 0 of column block cl
           // until its last use at ks = 8 cl + 9, then token half 1 (loaded 3 steps later).
           if (ks == 2) va[1] = vfrag(1, 0);
@@ -457,11 +578,13 @@ void attn_partial_h128(const AttnParams p) {
           if (ks == 28) va[2] = vfrag(2, 1);
           if (ks >= 30 && ks < 34) pb[1][ks - 30] = pfrag(ks - 30, 1);
           if (ks == 35) va[3] = vfrag(3, 1);
-          if (ks % 4 == 1) copy_row(tn, ks / 4, lo.ln);                             // ks = 1, 5, .., 33
+          if (!FP8 && ks % 4 == 1) copy_row(tn, ks / 4, lo.ln);                     // ks = 1, 5, .., 33
+          if (FP8 && ks % 8 == 1) copy_row(tn, ks / 8, lo.ln);                      // ks = 1, 9, .., 33
+          const bf16x8 ka = FP8 ? kop[ks % 2] : kq[ks % (kKPf + 1)];
           if (ks == 0)
-            score_mfma_first(s, kq[ks % (kKPf + 1)], qf[ks]);
+            score_mfma_first(s, ka, qf[ks]);
           else
-            score_mfma(s, kq[ks % (kKPf + 1)], qf[ks]);
+            score_mfma(s, ka, qf[ks]);
           if (ks >= 3 && ks % 2 == 1 && ks < 35) {
             const int a = (ks - 3) / 2;
             acc[a] = mfma32(va[a / 4], pb[0][a % 4], acc[a]);
@@ -473,6 +596,17 @@ void attn_partial_h128(const AttnParams p) {
         // 8(v/4) + 4h + v%4; tokens at or past `rem` (all, if the tile is not scored)
         // are masked.
         scores_ready(s);
+        // E4M3: the per-token scales of tile `it` for this lane's tokens 8 g + 4h + i; the
+        // key rows were widened without them, so they multiply the scores here and the
+        // probabilities below (value rows).
+        f32x4 tsc[4];
+        if constexpr (FP8) {
+          const uint32_t so = (uint32_t)offsetof(Smem<FP8>, sc) + ks3 * 256 + 16 * (lane_id_opaque() >> 5);
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) tsc[g4] = *(const f32x4*)((const unsigned char*)&sm + so + 32 * g4);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[v] *= tsc[v >> 2][v & 3];
+        }
         const int tt = t0 + it * kT;
         const int rem = cur ? end - tt : 0;
         if (rem < kT) {
@@ -504,6 +638,10 @@ void attn_partial_h128(const AttnParams p) {
           psum += x[v];
         }
         l_part += psum;
+        if constexpr (FP8) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) x[v] *= tsc[v >> 2][v & 3];
+        }
         // Token half `half` of this lane's probabilities is the B operand (head block
         // `wave`, token half `half`) of the accumulation: store it as is.
         unsigned char* pout = (unsigned char*)&sm + lo.pb + (it & 1) * kPBuf + wave * 2 * 1024;
@@ -604,10 +742,12 @@ void attn_partial_h128(const AttnParams p) {
 
 }  // namespace
 
-hipError_t launch_attn_h128(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_attn_h128(const AttnParams& p, bool fp8, hipStream_t stream) {
   if (p.n_h % kHeads != 0 || p.d_c != kDc || p.d_r != kDr) return hipErrorInvalidValue;
+  if (fp8 && (p.kv_scale == nullptr || p.new_c != nullptr)) return hipErrorInvalidValue;
   dim3 grid(p.num_splits, p.s_q * (p.n_h / kHeads));
-  return launch_attention_kernel(attn_partial_h128, grid, dim3(64 * kWaves), stream, p);
+  if (fp8) return launch_attention_kernel(attn_partial_h128<true>, grid, dim3(64 * kWaves), stream, p);
+  return launch_attention_kernel(attn_partial_h128<false>, grid, dim3(64 * kWaves), stream, p);
 }
 
 }  // namespace mla

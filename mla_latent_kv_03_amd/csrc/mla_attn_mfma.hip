@@ -425,8 +425,8 @@ __global__ __launch_bounds__(64 * (HB + kUWaves)) void attn_partial_split(const 
 int attn_heads_per_group(int n_h) { return n_h % 128 == 0 ? 128 : (n_h >= 64 ? 64 : n_h); }
 
 hipError_t launch_attn_mfma(const AttnParams& p, bool fp8, hipStream_t stream) {
+  if (p.n_h % 128 == 0) return launch_attn_h128(p, fp8, stream);   // all heads of a query position per workgroup
   if (fp8) return launch_attn_fp8_v0(p, stream);
-  if (p.n_h % 128 == 0) return launch_attn_h128(p, stream);   // all heads of a query position per workgroup
   const int hg = attn_heads_per_group(p.n_h);
   const int HB = hg / 16;
   dim3 grid(p.num_splits, p.s_q * (p.n_h / hg));

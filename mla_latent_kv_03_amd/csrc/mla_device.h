@@ -16,6 +16,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 #define MLA_LDS __attribute__((address_space(3)))
 
@@ -65,6 +66,22 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uin
                                                 void* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(lds_wave_base), 16, voffset, soffset, 0,
                                            kCachePolicyNT);
+}
+
+// The same copy, 4 bytes per lane: lane l's 4 bytes land at lds_wave_base + 4 * l.
+__device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t soffset,
+                                               void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(lds_wave_base), 4, voffset, soffset, 0,
+                                           kCachePolicyNT);
+}
+
+// Transposed 8-byte LDS read of 8-bit values: in each 16-lane block, lane 2r + q gives
+// the address of bytes 8q .. 8q+7 of row r (8 rows of 16 bytes); lane i of the block
+// receives byte i of rows 0..7, row r in byte r (lane layout measured on MI355X).
+__device__ __forceinline__ u32x2 lds_read_tr8(const void* p) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 __device__ __forceinline__ bf16x8 concat4(bf16x4 a, bf16x4 b) {

@@ -85,7 +85,7 @@ hipError_t launch_attention_kernel(Kernel kernel, dim3 grid, dim3 block, hipStre
 }
 
 hipError_t launch_attn_mfma(const AttnParams& p, bool fp8, hipStream_t stream);
-hipError_t launch_attn_h128(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_h128(const AttnParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_attn_fp8_v0(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
 hipError_t launch_combine_bf16(const CombineParams& p, hipStream_t stream);
