@@ -33,10 +33,12 @@ CSRC = os.path.join(ROOT, "mla_latent_kv_03_amd", "csrc")
 
 def attn_kernel(x):
     """(kernel name, source files) of the partial-attention kernel the library runs for workload x."""
-    if x.kv_dtype == "fp8":
-        return "attn_partial_mfma", ("mla_attn_mfma.hip", "mla_device.h", "mla_split.h")
+    fp8 = x.kv_dtype == "fp8"
     if x.n_h % 128 == 0:
-        return "attn_partial_h128", ("mla_attn_h128.hip", "mla_device.h", "mla_split.h")
+        return ("attn_partial_h128<true>" if fp8 else "attn_partial_h128<false>",
+                ("mla_attn_h128.hip", "mla_device.h", "mla_split.h"))
+    if fp8:
+        return "attn_partial_mfma<true>", ("mla_attn_fp8_v0.hip", "mla_device.h", "mla_split.h")
     return "attn_partial_split", ("mla_attn_mfma.hip", "mla_device.h", "mla_split.h")
 
 
