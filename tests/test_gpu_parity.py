@@ -128,13 +128,15 @@ def test_v3_long_fp8_b4_l131072():
 # ---------------------------------------------------------------- scores far above the first tile's
 
 @pytest.mark.parametrize("G", [0, 3])
-def test_late_dominant_token(G):
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_late_dominant_token(G, kv):
     """A token deep in the sequence whose scores exceed everything before it by far
     more than 2^64 (its latent is a large multiple of the heads' mean query direction):
-    softmax is dominated by it, and the kernels must still match the float64 oracle."""
-    _print_case("late_dominant_token", G=G)
+    softmax is dominated by it, and the kernels must still match the float64 oracle.
+    With an E4M3 cache the token's row is quantized with its own scale (30 / 448)."""
+    _print_case("late_dominant_token", G=G, kv=kv)
     import torch
-    x = workloads.make_decode([2049, 700], n_h=128, page_size=64, seed=77)
+    x = workloads.make_decode([2049, 700], n_h=128, page_size=64, kv_dtype=kv, seed=77)
     qdir = torch.sign(x.q_nope[0, 0].float().mean(dim=0))          # [d_c]
     for b, t in ((0, 1500), (1, 650)):
         slot = int(x.block_table[b, t // x.page_size]) * x.page_size + t % x.page_size
@@ -149,13 +151,14 @@ def test_late_dominant_token(G):
     compare_sampled(case, out, lse, [0, 1], tol, lse_tol=5e-3, what="late dominant token")
 
 
-def test_late_dominant_token_long_piece():
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_late_dominant_token_long_piece(kv):
     """One piece of 94 pages (a single split): the page-id window slides forward during
     the first pass, the dominant token at position 5500 forces a second pass, and that
     pass must start again from the piece's first pages."""
-    _print_case("late_dominant_token_long_piece", G=1)
+    _print_case("late_dominant_token_long_piece", G=1, kv=kv)
     import torch
-    x = workloads.make_decode([6000], n_h=128, page_size=64, seed=78)
+    x = workloads.make_decode([6000], n_h=128, page_size=64, kv_dtype=kv, seed=78)
     qdir = torch.sign(x.q_nope[0, 0].float().mean(dim=0))
     t = 5500
     slot = int(x.block_table[0, t // x.page_size]) * x.page_size + t % x.page_size
