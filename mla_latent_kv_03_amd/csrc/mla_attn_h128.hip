@@ -102,7 +102,10 @@ constexpr float kHeadroom = 64.f;             // tolerated excess over the refer
 
 template <bool FP8>
 struct Smem {
-  unsigned char v[kVRing][Layout<FP8>::kVTile];
+  union {
+    unsigned char v[kVRing][Layout<FP8>::kVTile];
+    unsigned char u_stage[kHeads][kDc * 2];   // epilogue: the piece's bf16 u, one 1 KiB row per head
+  };
   unsigned char k[kKRing][Layout<FP8>::kKTile];
   unsigned char p[2][kPBuf];                  // [tile % 2][head block][token half][lane] x 16 bytes
   float sc[FP8 ? kKRing : 1][64];             // E4M3: per-token scales of the tile (32 used)
@@ -241,13 +244,7 @@ void attn_partial_h128(const AttnParams p) {
     return o;
   };
 
-  const int len0 = first_lens(p.seq_lens, p.batch, p.max_tokens);   // in flight during the zeroing
-  // Ring slot 3 starts zeroed: the accumulation step that runs before a pass's first
-  // tile reads it with zero probabilities, and 0 * (stale bits) must not produce NaN.
-  // Afterwards the ring only ever holds cache rows or zeros.
-  for (int i = threadIdx.x; i < LT::kVTile / 16; i += 64 * kWaves)
-    ((u32x4*)sm.v[kVRing - 1])[i] = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();   // before any wave's first tile copies land in the ring
+  const int len0 = first_lens(p.seq_lens, p.batch, p.max_tokens);
 
   // The block-table row of the sequence this share starts in when all lengths are equal
   // is requested now, together with the lengths, instead of after the split walk (cold
@@ -256,6 +253,30 @@ void attn_partial_h128(const AttnParams p) {
   PageWindow pw;
   pw.init(p.block_table + (size_t)b_guess * p.max_pages, p.max_pages, p.num_pages, 0);
   int pw_b = b_guess;
+
+  // The queries of the guessed sequence are copied to LDS right away, one 1 KiB row per
+  // copy, so that their transfer overlaps the split walk; the first piece reads them back
+  // if its sequence is the guessed one.  (Loaded straight into the operand layout, each
+  // load instruction would touch 32 rows.)  16-byte chunk c of head row r is stored at
+  // c ^ (r % 16), of its RoPE row at c ^ ((r / 2) % 8), so that the operand reads (one
+  // chunk of 16 consecutive rows) are free of bank conflicts.  Wave w's rows go to
+  // u_stage rows 32w.. and to the probability buffers (4 KiB per wave), which nothing
+  // else uses before the first piece's tile copies.
+  {
+    const uint32_t lz = lane_id_opaque();
+    const size_t qrow0 = ((size_t)b_guess * p.s_q + q_pos) * p.n_h + head_base + 32 * wave;
+    const __amdgpu_buffer_rsrc_t qn = buffer_rsrc((const char*)p.q_nope + qrow0 * (kDc * 2));
+    const __amdgpu_buffer_rsrc_t qp = buffer_rsrc((const char*)p.q_pe + qrow0 * (kDr * 2));
+#pragma unroll 8
+    for (int r = 0; r < 32; ++r)
+      buffer_to_lds16(qn, (uint32_t)r * (kDc * 2) + 16u * (lz ^ (uint32_t)(r & 15)), 0u, sm.u_stage[32 * wave + r]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t r = 8u * j + (lz >> 3);
+      buffer_to_lds16(qp, r * (kDr * 2) + 16u * ((lz & 7u) ^ ((r >> 1) & 7u)), 0u, (unsigned char*)sm.p + wave * 4096 + j * 1024);
+    }
+  }
+  bool first_piece = true;
 
   // Fused append, pool write of new row `wave` of sequence w (row group 0), at the start:
   // the wait for its load overlaps the wait for the lengths that the split walk makes
@@ -322,6 +343,22 @@ void attn_partial_h128(const AttnParams p) {
         for (int ks = 0; ks < kQkV; ++ks) qf[ks] = *(const bf16x8*)(qn + 32 * (ks >> 1) + 8 * (ks & 1));
 #pragma unroll
         for (int kk = 0; kk < kQk - kQkV; ++kk) qf[kQkV + kk] = *(const bf16x8*)(qp + 32 * (kk >> 1) + 8 * (kk & 1));
+      }
+    };
+    // The queries from the LDS copy made at kernel entry (same layout as load_queries).
+    auto read_staged_queries = [&]() {
+      const uint32_t ql = lane_id_opaque(), l32 = ql & 31u, h = ql >> 5;
+      const unsigned char* qrow = sm.u_stage[32 * wave + (int)l32];
+      const unsigned char* prow = (const unsigned char*)sm.p + wave * 4096 + l32 * (kDr * 2);
+#pragma unroll
+      for (int ks = 0; ks < kQk; ++ks) {
+        // logical 16-byte chunk of the row that k-step ks reads
+        const uint32_t c = !FP8 ? 2u * (uint32_t)(ks < kQkV ? ks : ks - kQkV) + h
+                                : 4u * (uint32_t)((ks < kQkV ? ks : ks - kQkV) >> 1) + 2u * h + (uint32_t)(ks & 1);
+        if (ks < kQkV)
+          qf[ks] = *(const bf16x8*)(qrow + 16u * (c ^ (l32 & 15u)));
+        else
+          qf[ks] = *(const bf16x8*)(prow + 16u * (c ^ ((l32 >> 1) & 7u)));
       }
     };
     const int tiles_per_page = p.page_size / kT;
@@ -431,6 +468,23 @@ void attn_partial_h128(const AttnParams p) {
         for (int v = 0; v < 16; ++v) acc[a][v] = 0.f;
       l_part = 0.f;
       x_max = -INFINITY;
+      if (first_pass && first_piece) {
+        // The query copies made at kernel entry must land before the ring and the
+        // probability buffers are reused; read them back if they are this piece's.
+        wait_vmcnt<0>();
+        if (pc.b == b_guess) read_staged_queries();
+        lds_barrier();
+      }
+      if (first_pass) {
+        // Ring slot 3 is zeroed for each piece: the accumulation step that runs before a
+        // pass's first tile reads it with zero probabilities, and 0 * (stale bits) must
+        // not produce NaN; before the first piece it holds queries, afterwards the
+        // previous piece's staged u (not valid E4M3 codes).  Within the piece the ring
+        // only holds cache rows or zeros.  (The first iteration's barrier orders these
+        // writes before those reads.)
+        for (int i = threadIdx.x; i < LT::kVTile / 16; i += 64 * kWaves)
+          ((u32x4*)sm.v[kVRing - 1])[i] = u32x4{0u, 0u, 0u, 0u};
+      }
       // Zero probabilities of "tile -1" (buffer 1), this wave's head block.
 #pragma unroll
       for (int half = 0; half < 2; ++half)
@@ -467,7 +521,7 @@ void attn_partial_h128(const AttnParams p) {
         ready |= ok ? (1u << t) : 0u;
 #pragma unroll
         for (int j = 0; j < LT::kCopies; ++j) copy_row(tc, j, lz0);
-        if (t == 0 && first_pass) load_queries();
+        if (t == 0 && first_pass && !(first_piece && pc.b == b_guess)) load_queries();
       }
       int vs = 0, ks3 = 0;   // ring slots of tile `it`
       for (int it = 0; it <= ntiles; ++it) {
@@ -693,26 +747,43 @@ void attn_partial_h128(const AttnParams p) {
       sm.l[32 * wave + l32] = l_tot;
       p.part_lse[row_base + 32 * wave + l32] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
+    // Every copy has landed (the barrier waits for all of this wave's memory operations),
+    // so the tile ring is free: each wave stages its columns of u for every head there
+    // (16-byte chunk c of head row r at c ^ (r % 16)), and then writes 32 whole head rows,
+    // one 1 KiB store each; stores straight from the accumulator layout would write 16
+    // bytes of 32 different rows per instruction.
     __syncthreads();
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
       const float lt = sm.l[32 * hb + l32];
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      bf16* up = (bf16*)p.part_u + (row_base + 32 * hb + l32) * kDc + 128 * wave + 4 * h;
+      const int r = 32 * hb + l32;
+      unsigned char* srow = sm.u_stage[r] + 8 * h;
 #pragma unroll
       for (int cl = 0; cl < 4; ++cl)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          __builtin_amdgcn_sched_barrier(0);
           f32x4 o;
 #pragma unroll
           for (int k = 0; k < 4; ++k) o[k] = acc[4 * cl + hb][4 * g4 + k] * inv;
-          *(bf16x4*)(up + 32 * cl + 8 * g4) = to_bf16x4(o);
+          const int c = 16 * wave + 4 * cl + g4;
+          *(bf16x4*)(srow + 16 * (c ^ (r & 15))) = to_bf16x4(o);
         }
+    }
+    __syncthreads();
+    {
+      const uint32_t l = lane_id_opaque();
+      unsigned char* ub = (unsigned char*)p.part_u + (row_base + 32 * wave) * (kDc * 2) + 16 * l;
+#pragma unroll 4
+      for (int i = 0; i < 32; ++i) {
+        const int r = 32 * wave + i;
+        *(u32x4*)(ub + i * (kDc * 2)) = *(const u32x4*)(sm.u_stage[r] + 16 * (l ^ (uint32_t)(r & 15)));
+      }
     }
     // The next piece's prologue refills ring slots 0 and 1, the row sums and the stash,
     // which other waves may still be reading for this piece.
     __syncthreads();
+    first_piece = false;
   });
 
   // Fused append: the rest of this share's pool writes (sequences w + G, w + 2G, ..).  No
