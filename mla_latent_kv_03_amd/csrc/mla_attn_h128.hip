@@ -195,6 +195,11 @@ void attn_partial_h128(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) Smem<FP8> sm;
   using LT = Layout<FP8>;
 
+  // Every 64-byte line of the argument block is read here, in one batch: a scalar-cache
+  // miss on it is a memory round trip, and the compiler would otherwise first touch the
+  // later lines where they are used, one round trip after another.
+  asm volatile("" ::"s"(p.q_nope), "s"(p.c_stride), "s"(p.split_table), "s"(p.s_new));
+
   // Consecutive shares (the pieces of one sequence) on one XCD: workgroups are dispatched
   // to the 8 XCDs round-robin, so workgroup i takes share (i % 8) * (G / 8) + i / 8.
   const int w = p.num_splits % 8 == 0 ? (int)(blockIdx.x % 8) * (p.num_splits / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
@@ -246,10 +251,21 @@ void attn_partial_h128(const AttnParams p) {
 
   const int len0 = first_lens(p.seq_lens, p.batch, p.max_tokens);
 
+  // New row of the fused append that this wave writes to the pool at the start (below).
+  const int fused_row = kWaves - 1 - wave;
+  const bool fused_write = p.new_c != nullptr && rg == 0 && w < p.batch && fused_row < p.s_new;
+  u32x4 new_c_row = u32x4{0u, 0u, 0u, 0u}, new_k_row = u32x4{0u, 0u, 0u, 0u};
+  if (!FP8 && fused_write) {
+    const uint32_t l = lane_id_opaque();
+    const size_t tok = (size_t)w * p.s_new + fused_row;
+    new_c_row = *(const u32x4*)((const char*)p.new_c + tok * kDc * 2 + 16 * l);
+    new_k_row = *(const u32x4*)((const char*)p.new_k + tok * kDr * 2 + 16 * (l % (kKRow / 16)));
+  }
+
   // The block-table row of the sequence this share starts in when all lengths are equal
   // is requested now, together with the lengths, instead of after the split walk (cold
   // loads take microseconds); a piece of another sequence loads its own row.
-  const int b_guess = min(p.batch - 1, (int)(((long long)w * p.batch) / p.num_splits));
+  const int b_guess = min(p.batch - 1, (int)udiv_mostly32((unsigned long long)w * (unsigned)p.batch, (unsigned)p.num_splits));
   PageWindow pw;
   pw.init(p.block_table + (size_t)b_guess * p.max_pages, p.max_pages, p.num_pages, 0);
   int pw_b = b_guess;
@@ -267,7 +283,7 @@ void attn_partial_h128(const AttnParams p) {
     const size_t qrow0 = ((size_t)b_guess * p.s_q + q_pos) * p.n_h + head_base + 32 * wave;
     const __amdgpu_buffer_rsrc_t qn = buffer_rsrc((const char*)p.q_nope + qrow0 * (kDc * 2));
     const __amdgpu_buffer_rsrc_t qp = buffer_rsrc((const char*)p.q_pe + qrow0 * (kDr * 2));
-#pragma unroll 8
+#pragma unroll
     for (int r = 0; r < 32; ++r)
       buffer_to_lds16(qn, (uint32_t)r * (kDc * 2) + 16u * (lz ^ (uint32_t)(r & 15)), 0u, sm.u_stage[32 * wave + r]);
 #pragma unroll
@@ -278,25 +294,22 @@ void attn_partial_h128(const AttnParams p) {
   }
   bool first_piece = true;
 
-  // Fused append, pool write of new row `wave` of sequence w (row group 0), at the start:
-  // the wait for its load overlaps the wait for the lengths that the split walk makes
-  // anyway (sequences w + G, w + 2G, .. are written at the end of the launch).  The
-  // stores' completion is never waited for: the tile loop's copy waits only ever count
-  // them as outstanding, which makes those waits stricter, not weaker.
-  if (p.new_c != nullptr && rg == 0 && w < p.batch && wave < p.s_new) {
+  // Fused append, pool write of new row i of sequence w (row group 0) by wave
+  // kWaves - 1 - i, at the start (sequences w + G, w + 2G, .. are written at the end of
+  // the launch).  The row is loaded before the query copies are issued, and the position
+  // and page lookups go through the scalar cache, so that no wait of this write waits
+  // for the query copies.  The stores' completion is never waited for: the tile loop's
+  // copy waits only ever count them as outstanding, which makes those waits stricter.
+  if (!FP8 && fused_write) {
     const uint32_t l = lane_id_opaque();
-    const int tok = w * p.s_new + wave;
-    const u32x4 nc = *(const u32x4*)((const char*)p.new_c + (size_t)tok * kDc * 2 + 16 * l);
-    u32x4 nk = u32x4{0u, 0u, 0u, 0u};
-    if (l < kKRow / 16) nk = *(const u32x4*)((const char*)p.new_k + (size_t)tok * kDr * 2 + 16 * l);
-    const int pos = p.new_pos[tok];
+    const int pos = load_scalar(p.new_pos + (size_t)w * p.s_new + fused_row);
     if (pos >= 0 && pos / p.page_size < p.max_pages) {
-      const int page = p.block_table[(size_t)w * p.max_pages + pos / p.page_size];
+      const int page = load_scalar(p.block_table + (size_t)w * p.max_pages + pos / p.page_size);
       if (page >= 0 && page < p.num_pages) {
         const size_t slot = (size_t)page * p.page_size + pos % p.page_size;
-        *(u32x4*)((char*)const_cast<void*>(p.c_kv) + slot * ((size_t)p.c_stride * 2) + 16 * l) = nc;
+        *(u32x4*)((char*)const_cast<void*>(p.c_kv) + slot * ((size_t)p.c_stride * 2) + 16 * l) = new_c_row;
         if (l < kKRow / 16)
-          *(u32x4*)((char*)const_cast<void*>(p.k_pe) + slot * ((size_t)p.k_stride * 2) + 16 * l) = nk;
+          *(u32x4*)((char*)const_cast<void*>(p.k_pe) + slot * ((size_t)p.k_stride * 2) + 16 * l) = new_k_row;
       }
     }
   }

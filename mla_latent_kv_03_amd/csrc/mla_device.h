@@ -68,6 +68,13 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uin
                                            kCachePolicyNT);
 }
 
+// A load through the scalar cache (the address must be wave-uniform, and the memory must
+// not be written while the kernel runs): its wait is counted apart from the vector-memory
+// operations, so it never waits for copies in flight.
+__device__ __forceinline__ int32_t load_scalar(const int32_t* ptr) {
+  return *(const __attribute__((address_space(4))) int32_t*)ptr;
+}
+
 // The same copy, 4 bytes per lane: lane l's 4 bytes land at lds_wave_base + 4 * l.
 __device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t soffset,
                                                void* lds_wave_base) {

@@ -29,6 +29,9 @@ __device__ __forceinline__ int clamp_len(int L, int max_tokens) {
   return L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
 }
 
+// Units of a clamped length (at most 2^25, so a sum over 64 sequences fits 32 bits).
+__device__ __forceinline__ unsigned units_of(int L) { return ((unsigned)L + (kSplitUnit - 1)) / kSplitUnit; }
+
 // Exclusive prefix sum of v over the workgroup (blockDim.x a multiple of 64, <= 1024).
 // Every thread must call it; `total` receives the workgroup sum.
 __device__ inline long long block_exclusive_scan(long long v, SplitScratch* s, long long& total) {
@@ -66,7 +69,7 @@ __device__ void for_each_piece(const int32_t* __restrict__ seq_lens, int B, int 
                                int32_t* __restrict__ table, SplitScratch* s, Piece* pieces, F&& process) {
   const int nt = blockDim.x, tid = threadIdx.x;
   long long local = 0;
-  for (int b = tid; b < B; b += nt) local += (clamp_len(seq_lens[b], max_tokens) + kSplitUnit - 1) / kSplitUnit;
+  for (int b = tid; b < B; b += nt) local += units_of(clamp_len(seq_lens[b], max_tokens));
   long long total;
   (void)block_exclusive_scan(local, s, total);
   if (total == 0) {
@@ -82,7 +85,7 @@ __device__ void for_each_piece(const int32_t* __restrict__ seq_lens, int B, int 
   for (int base = 0; base < B; base += nt) {
     const int b = base + tid;
     const int L = b < B ? clamp_len(seq_lens[b], max_tokens) : 0;
-    const long long n = (L + kSplitUnit - 1) / kSplitUnit;
+    const long long n = units_of(L);
     long long chunk_total;
     const long long start = carry + block_exclusive_scan(n, s, chunk_total);
     if (table && b < B && b % G == w) {
@@ -127,29 +130,35 @@ __device__ __forceinline__ uint32_t lane_id_opaque() {
   return l;
 }
 
-__device__ __forceinline__ long long wave_inclusive_scan(long long x) {
-  const int lane = (int)lane_id_opaque();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int src = (lane >= d ? lane - d : lane) << 2;
-    const unsigned lo = (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)(unsigned)(unsigned long long)x);
-    const unsigned hi = (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)(unsigned)((unsigned long long)x >> 32));
-    if (lane >= d) x += (long long)(((unsigned long long)hi << 32) | lo);
-  }
+// Inclusive prefix sum over the 64 lanes of a wave, in 32 bits: sums within each row of
+// 16 lanes by DPP row shifts of 1, 2, 4 and 8 lanes, then the totals of rows 0 and 2 are
+// broadcast into rows 1 and 3, and the total of rows 0-1 into rows 2 and 3.  Lanes that a
+// shift or broadcast does not reach take 0.  (Six dependent VALU steps instead of six
+// rounds of cross-lane permutes through LDS.)
+__device__ __forceinline__ unsigned wave_inclusive_scan_u32(unsigned x) {
+  x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
 }
 
-__device__ __forceinline__ long long wave_total(long long x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
-  return x;
-}
-
-// The clamped length of sequence `lane` (0 past the batch): the first 64 lengths, which
-// a kernel can load before other set-up work and hand to for_each_piece_wave.
+// Lengths of sequences 0..63 as loaded (not clamped; lanes past the batch read sequence
+// B - 1), which a kernel can request before other set-up work and hand to
+// for_each_piece_wave.  The load is unconditional so that nothing waits for it before
+// the walk uses it (a load under a lane condition is waited for where the branch joins).
 __device__ __forceinline__ int first_lens(const int32_t* __restrict__ seq_lens, int B, int max_tokens) {
+  (void)max_tokens;
   const int lane = threadIdx.x & 63;
-  return lane < B ? clamp_len(seq_lens[lane], max_tokens) : 0;
+  return seq_lens[lane < B ? lane : B - 1];
+}
+
+// Quotient of 64-bit values that usually fit in 32 bits (the 32-bit division is a few
+// instructions, the 64-bit one a long software sequence).
+__device__ __forceinline__ unsigned long long udiv_mostly32(unsigned long long a, unsigned long long d) {
+  return (a | d) >> 32 ? a / d : (unsigned long long)((unsigned)a / (unsigned)d);
 }
 
 // Same rule as for_each_piece, evaluated by each wave on its own (64 sequences per
@@ -168,66 +177,62 @@ __device__ void for_each_piece_wave(const int32_t* __restrict__ seq_lens, int B,
   const int lane = threadIdx.x & 63;
   auto len_of = [&](int base) {
     const int b = base + lane;
-    return base == 0 ? len0 : (b < B ? clamp_len(seq_lens[b], max_tokens) : 0);
+    const int raw = base == 0 ? len0 : seq_lens[b < B ? b : B - 1];
+    return b < B ? clamp_len(raw, max_tokens) : 0;
   };
-  // Uniform values are kept in scalar registers.
-  auto uniform64 = [](long long v) {
-    const unsigned lo32 = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long long)v);
-    const unsigned hi32 = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)v >> 32));
-    return (long long)(((unsigned long long)hi32 << 32) | lo32);
-  };
-  long long total = 0;
-  for (int base = 0; base < B; base += 64) total += wave_total((len_of(base) + kSplitUnit - 1) / kSplitUnit);
-  total = uniform64(total);
-  const long long share = total > 0 ? (total + G - 1) / G : 1;
-  const long long lo = (long long)w * share;
-  const long long hi = lo + share < total ? lo + share : total;
+  auto wave_sum = [](unsigned incl) { return (unsigned)__builtin_amdgcn_readlane((int)incl, 63); };
+  unsigned long long total = 0;
+  for (int base = 0; base < B; base += 64) total += wave_sum(wave_inclusive_scan_u32(units_of(len_of(base))));
+  const unsigned long long share = total > 0 ? udiv_mostly32(total - 1, (unsigned)G) + 1 : 1;
+  const unsigned long long lo = (unsigned long long)w * share;
+  const unsigned long long hi = lo + share < total ? lo + share : total;
 
   if (table) {
-    long long carry = 0;
+    unsigned long long carry = 0;
     for (int base = 0; base < B; base += 64) {
       const int b = base + lane;
-      const long long n = (len_of(base) + kSplitUnit - 1) / kSplitUnit;
-      const long long incl = wave_inclusive_scan(n);
-      const long long start = carry + incl - n;
-      if (b < B && b % G == w) {
+      const unsigned n = units_of(len_of(base));
+      const unsigned incl = wave_inclusive_scan_u32(n);
+      const unsigned long long start = carry + (incl - n);
+      if (b < B && (unsigned)b % (unsigned)G == (unsigned)w) {
         int first = 0, cnt = 0;
         if (n > 0) {
-          const long long wf = start / share, wl = (start + n - 1) / share;
+          const unsigned long long wf = udiv_mostly32(start, share), wl = udiv_mostly32(start + n - 1, share);
           first = (int)wf + b;
           cnt = (int)(wl - wf + 1);
         }
         table[2 * b] = first;
         table[2 * b + 1] = cnt;
       }
-      carry += uniform64(__shfl(incl, 63, 64));
+      carry += wave_sum(incl);
     }
   }
   if (total == 0) return;
 
   // First piece of share w in a sequence after `after`; false if there is none.
   auto next_piece = [&](int after, Piece& pc) {
-    long long carry = 0;
+    unsigned long long carry = 0;
     for (int base = 0; base < B; base += 64) {
       const int b = base + lane;
       const int L = len_of(base);
-      const long long n = (L + kSplitUnit - 1) / kSplitUnit;
-      const long long incl = wave_inclusive_scan(n);
-      const long long start = carry + incl - n;
+      const unsigned n = units_of(L);
+      const unsigned incl = wave_inclusive_scan_u32(n);
+      const unsigned long long start = carry + (incl - n);
       const bool mine = b > after && n > 0 && start < hi && start + n > lo;
       const unsigned long long mask = __ballot(mine);
       if (mask) {
         const int src = __builtin_ctzll(mask);
-        const long long u0 = (lo > start ? lo : start) - start;
-        const long long u1 = (hi < start + n ? hi : start + n) - start;
+        const unsigned u0 = (unsigned)((lo > start ? lo : start) - start);
+        const unsigned u1 = (unsigned)((hi < start + n ? hi : start + n) - start);
+        const unsigned long long e = (unsigned long long)u1 * kSplitUnit;
         pc.b = base + src;
         pc.t0 = __builtin_amdgcn_readlane((int)(u0 * kSplitUnit), src);
-        pc.t1 = __builtin_amdgcn_readlane((int)(u1 * kSplitUnit < L ? u1 * kSplitUnit : L), src);
+        pc.t1 = __builtin_amdgcn_readlane(e < (unsigned long long)L ? (int)e : L, src);
         pc.len = __builtin_amdgcn_readlane(L, src);
         pc.slot = w + pc.b;
         return true;
       }
-      carry += uniform64(__shfl(incl, 63, 64));
+      carry += wave_sum(incl);
       if (carry >= hi) break;
     }
     return false;
