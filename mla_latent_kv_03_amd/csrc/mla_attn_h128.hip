@@ -751,21 +751,26 @@ void attn_partial_h128(const AttnParams p) {
     if (redo) {
       m_ref += max_xor32(x_max);
       run_pass(false);
+      wait_vmcnt<0>();
     }
+    // No copy is in flight now (the vote's barrier waited for all of this wave's memory
+    // operations, the redo pass ends with the same wait), so the tile ring is free.
 
-    // Epilogue: u = U / l.  Row sums go through LDS to the column-owning waves.
+    // Epilogue: u = U / l.  Row sums go through LDS to the column-owning waves; the
+    // barriers from here on wait for LDS operations only, never for the stores.
     const int el = (int)lane_id_opaque(), l32 = el & 31, h = el >> 5;
     const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
     if (h == 0) {
       sm.l[32 * wave + l32] = l_tot;
       p.part_lse[row_base + 32 * wave + l32] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
-    // Every copy has landed (the barrier waits for all of this wave's memory operations),
-    // so the tile ring is free: each wave stages its columns of u for every head there
-    // (16-byte chunk c of head row r at c ^ (r % 16)), and then writes 32 whole head rows,
-    // one 1 KiB store each; stores straight from the accumulator layout would write 16
-    // bytes of 32 different rows per instruction.
-    __syncthreads();
+    lds_barrier();
+    // One head block at a time, each wave stages its columns of u for the block's 32
+    // heads in the ring (16-byte chunk c of head row r at c ^ (r % 16)) and, after a
+    // barrier, writes 8 whole rows of the block, one 1 KiB store each, while the next
+    // block is staged; stores straight from the accumulator layout would write 16 bytes
+    // of 32 different rows per instruction.
+    const uint32_t el_u = lane_id_opaque();
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
       const float lt = sm.l[32 * hb + l32];
@@ -782,20 +787,17 @@ void attn_partial_h128(const AttnParams p) {
           const int c = 16 * wave + 4 * cl + g4;
           *(bf16x4*)(srow + 16 * (c ^ (r & 15))) = to_bf16x4(o);
         }
-    }
-    __syncthreads();
-    {
-      const uint32_t l = lane_id_opaque();
-      unsigned char* ub = (unsigned char*)p.part_u + (row_base + 32 * wave) * (kDc * 2) + 16 * l;
-#pragma unroll 4
-      for (int i = 0; i < 32; ++i) {
-        const int r = 32 * wave + i;
-        *(u32x4*)(ub + i * (kDc * 2)) = *(const u32x4*)(sm.u_stage[r] + 16 * (l ^ (uint32_t)(r & 15)));
+      lds_barrier();
+      unsigned char* ub = (unsigned char*)p.part_u + (row_base + 32 * hb + 8 * wave) * (kDc * 2) + 16 * el_u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rr = 32 * hb + 8 * wave + i;
+        *(u32x4*)(ub + i * (kDc * 2)) = *(const u32x4*)(sm.u_stage[rr] + 16 * (el_u ^ (uint32_t)(rr & 15)));
       }
     }
     // The next piece's prologue refills ring slots 0 and 1, the row sums and the stash,
     // which other waves may still be reading for this piece.
-    __syncthreads();
+    lds_barrier();
     first_piece = false;
   });
 
