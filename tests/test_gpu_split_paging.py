@@ -38,6 +38,35 @@ def test_partials_and_split_table(kv):
         assert np.max(np.abs(plse_h[slot, 0] - lse_ref)) <= (1e-5 if kv == "f32" else 5e-3)
 
 
+@pytest.mark.parametrize("B,G,seed", [(64, 256, 11), (65, 7, 12), (130, 256, 13), (200, 64, 14), (130, 1, 15)])
+def test_split_table_across_wave_steps(B, G, seed):
+    """The device split walk takes 64 sequences per scan step: batches of one, two and four
+    steps, zero lengths among them, and share counts below, at and above the batch."""
+    _print_case("split walk", B=B, G=G, seed=seed)
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 260, size=B)
+    lens[rng.random(B) < 0.15] = 0
+    lens[rng.integers(0, B, size=3)] = [1500, 64, 65]
+    lens = [int(v) for v in lens]
+    x = workloads.make_decode(lens, page_size=64, kv_dtype="bf16", q_dtype="bf16", seed=seed + 100,
+                              n_h=128, d_c=512, d_r=64, d_v=128)
+    case = DeviceCase(x, num_splits=G)
+    _, _, ws = case.run(partials_only=True)
+    table, plse, pu = case.binding.workspace_views(case.params, ws)
+    want_table, pieces = ref.split_table(lens, G)
+    assert np.array_equal(table.cpu().numpy(), want_table), "split table differs"
+    # A sample of pieces, most of them past the first 64 sequences, against the oracle.
+    qn, qp = x.q_nope.double().numpy(), x.q_pe.double().numpy()
+    plse_h, pu_h = plse.cpu().numpy(), pu.float().cpu().numpy()
+    late = [pc for pc in pieces if pc[0] >= 64] or pieces
+    sample = [pieces[0], pieces[-1]] + [late[i] for i in rng.choice(len(late), size=min(4, len(late)), replace=False)]
+    for (b, w, slot, t0, t1) in sample:
+        c, kp = case.rows_of(b)
+        u_ref, lse_ref = ref.split_partial(qn[b, 0], qp[b, 0], c, kp, x.softmax_scale, t0, t1)
+        assert_close(pu_h[slot, 0], u_ref, BF16_TOL, f"partial u b={b} slot={slot} tokens [{t0}, {t1})")
+        assert np.max(np.abs(plse_h[slot, 0] - lse_ref)) <= 5e-3, f"partial lse b={b} slot={slot}"
+
+
 @pytest.mark.parametrize("kv", ["bf16", "f32"])
 def test_standalone_combine_on_oracle_partials(kv):
     """Partials of an arbitrary partition (oracle-made) merged by mla_decode_splitkv_combine."""
