@@ -788,11 +788,14 @@ void attn_partial_h128(const AttnParams p) {
           *(bf16x4*)(srow + 16 * (c ^ (r & 15))) = to_bf16x4(o);
         }
       lds_barrier();
-      unsigned char* ub = (unsigned char*)p.part_u + (row_base + 32 * hb + 8 * wave) * (kDc * 2) + 16 * el_u;
+      // Written through the L2: the combine launch reads these rows, and left dirty they
+      // would be written back at the end of this launch, after its last workgroup.
+      const __amdgpu_buffer_rsrc_t ur = buffer_rsrc((const char*)p.part_u + (row_base + 32 * hb + 8 * wave) * (kDc * 2));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int rr = 32 * hb + 8 * wave + i;
-        *(u32x4*)(ub + i * (kDc * 2)) = *(const u32x4*)(sm.u_stage[rr] + 16 * (el_u ^ (uint32_t)(rr & 15)));
+        buffer_store16(*(const u32x4*)(sm.u_stage[rr] + 16 * (el_u ^ (uint32_t)(rr & 15))), ur,
+                       16 * el_u + (uint32_t)i * (kDc * 2), kCachePolicyWriteThrough);
       }
     }
     // The next piece's prologue refills ring slots 0 and 1, the row sums and the stash,

@@ -43,6 +43,17 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
 // (measured on MI355X: about 3.9 -> 6.9 TB/s).
 constexpr int kCachePolicyNT = 2;
 
+// Cache-policy bits "sc0 sc1" (system scope) of a store: the data is written through the
+// L2 instead of staying there dirty until the write-back at the end of the launch.  For
+// output that a later launch reads, written at the end of a kernel, this moves the
+// write-back off the launch's tail.
+constexpr int kCachePolicyWriteThrough = 17;
+
+// 16-byte store through a buffer resource: lane l writes base + voffset_l.
+__device__ __forceinline__ void buffer_store16(u32x4 v, __amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, int policy) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, (int)voffset, 0, policy);
+}
+
 // 16-byte global -> LDS copy without a register round trip: lane l's 16 bytes land
 // at lds_wave_base + 16 * l (lds_wave_base must be wave-uniform).  Streaming policy.
 __device__ __forceinline__ void global_to_lds16(const void* gsrc, void* lds_wave_base) {
