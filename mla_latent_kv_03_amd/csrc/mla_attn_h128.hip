@@ -794,8 +794,8 @@ void attn_partial_h128(const AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int rr = 32 * hb + 8 * wave + i;
-        buffer_store16(*(const u32x4*)(sm.u_stage[rr] + 16 * (el_u ^ (uint32_t)(rr & 15))), ur,
-                       16 * el_u + (uint32_t)i * (kDc * 2), kCachePolicyWriteThrough);
+        buffer_store16<kCachePolicyWriteThrough>(*(const u32x4*)(sm.u_stage[rr] + 16 * (el_u ^ (uint32_t)(rr & 15))),
+                                                 ur, 16 * el_u + (uint32_t)i * (kDc * 2));
       }
     }
     // The next piece's prologue refills ring slots 0 and 1, the row sums and the stash,

@@ -50,8 +50,9 @@ constexpr int kCachePolicyNT = 2;
 constexpr int kCachePolicyWriteThrough = 17;
 
 // 16-byte store through a buffer resource: lane l writes base + voffset_l.
-__device__ __forceinline__ void buffer_store16(u32x4 v, __amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, int policy) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, (int)voffset, 0, policy);
+template <int kPolicy>
+__device__ __forceinline__ void buffer_store16(u32x4 v, __amdgpu_buffer_rsrc_t rsrc, uint32_t voffset) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, (int)voffset, 0, kPolicy);
 }
 
 // 16-byte global -> LDS copy without a register round trip: lane l's 16 bytes land
