@@ -28,6 +28,8 @@ METRIC = "MLA decode latent-KV tokens/s + achieved HBM GB/s & MFMA % of peak"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_partial_traffic.json")
+MI355X_SIMDS = 1024             # 256 CUs x 4 SIMDs (8 XCDs)
+MI355X_XCDS = 8
 CSRC = os.path.join(ROOT, "mla_latent_kv_03_amd", "csrc")
 
 
@@ -262,9 +264,17 @@ def cpu_baseline(x, budget_s=12.0):
                       f"{passes} pass(es) over the batch), float64 NumPy absorbed-form oracle, {spent:.1f} s"}
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+
+
 def pmc_summary(args):
     """Attention-kernel HBM traffic from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by the
-    ratio the same counter shows for the plain copy kernel of known size in the same run."""
+    ratio the same counter shows for the plain copy kernel of known size in the same run.  If one of the
+    result databases also holds SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 for the attention kernel, the record also gets the matrix unit's busy
+    fraction (busy cycles summed over all SIMDs / (active cycles per XCD x SIMDs); the database holds
+    GRBM_GUI_ACTIVE summed over the XCDs) and the counted bf16 MFMA flops (512 per MOP), medians
+    over the dispatches."""
     import sqlite3
     kname, ksrc = attn_kernel(make_workload(args.workload))
     vals = {}   # (kernel kind, counter) -> per-dispatch totals
@@ -276,7 +286,7 @@ def pmc_summary(args):
         for r in db.execute("select * from counters_collection"):
             name, ctr = r[ci["kernel_name"]], r[ci["counter_name"]]
             kind = "attn" if kname in name else ("copy" if "neg_kernel" in name else None)
-            if kind is None or ctr not in ("FETCH_SIZE", "WRITE_SIZE"):
+            if kind is None or ctr not in ("FETCH_SIZE", "WRITE_SIZE") + MFMA_COUNTERS:
                 continue
             key = (kind, ctr, path, r[ci["dispatch_id"]])
             per[key] = per.get(key, 0.0) + float(r[ci["value"]])
@@ -296,6 +306,14 @@ def pmc_summary(args):
            "copy_factor_fetch": round(f_read, 4), "copy_factor_write": round(f_write, 4),
            "attn_dispatches": len(vals[("attn", "FETCH_SIZE")]), "command": args.pmc_command,
            "kernel": kname, "source_digest": source_digest(ksrc)}
+    if all(("attn", c) in vals for c in MFMA_COUNTERS):
+        import statistics
+        busy, active, mops = (vals[("attn", c)] for c in MFMA_COUNTERS)
+        frac = [b / (a / MI355X_XCDS * MI355X_SIMDS) for b, a in zip(busy, active)]
+        rec["mfma_busy_frac"] = round(statistics.median(frac), 4)
+        rec["mfma_counted_flops"] = round(statistics.median(mops) * 512)
+        print(f"workload {args.workload}: MFMA busy {rec['mfma_busy_frac']:.1%} of active SIMD cycles, "
+              f"{rec['mfma_counted_flops'] / 1e9:.2f} GFLOP counted per launch")
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     data = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
     data[args.workload] = rec
@@ -391,16 +409,23 @@ def main():
     attn_gbs = alg["attn_bytes"] / (attn_ms * 1e-3) / 1e9
     attn_tflops = alg["attn_flops"] / (attn_ms * 1e-3) / 1e12
     traffic = None
+    counted = {}
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE)).get(args.workload)
         # Counters taken on another kernel, or on an older source of this one, do not count.
         if rec and rec.get("kernel") == kname and rec.get("source_digest") == source_digest(ksrc):
             traffic = rec.get("bytes_per_launch")
+            # The same bytes over this run's kernel time, and the matrix unit's busy fraction
+            # from the counters of the profiled run.
+            counted["traffic_gbs"] = round(traffic / (attn_ms * 1e-3) / 1e9, 1)
+            if "mfma_busy_frac" in rec:
+                counted["mfma_busy_frac_counter"] = rec["mfma_busy_frac"]
     roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": kname, "kernel_us": round(attn_ms * 1e3, 2),
             "mfma_tflops": round(attn_tflops, 1), "mfma_frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
-            "algorithmic_bytes_per_launch": alg["attn_bytes"], "algorithmic_flops_per_launch": alg["attn_flops"]}
+            "algorithmic_bytes_per_launch": alg["attn_bytes"], "algorithmic_flops_per_launch": alg["attn_flops"],
+            **counted}
     result = {
         "metric": METRIC, "value": round(alg["tokens"] / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
