@@ -30,7 +30,10 @@ Readings where the pages are silent or garbled (numbered as in the design notes)
 
 Pins (each function is checked by something other than itself, see tests/):
   rope               hand-computed rotations; relative-position invariance; norm.
-  project_tiny,
+  project_tiny       scalar-loop recomputation of c = W^DKV h, q^C = W^Q h, both rotations
+                     (complex exponentials at the token's own position) and every score
+                     term q^R_{t,i} . k^R_j from the unrotated projections
+                     (tests/test_oracle_projections.py; planted mutants caught).
   mla_nonabsorbed    absorbed == non-absorbed identity; pure-Python brute force.
   mla_absorbed       torch SDPA in float64; brute force; closed forms.
   split_partial,

@@ -183,3 +183,45 @@ def test_fp8_mutant_caught():
 
     assert [half_away(float(v)) for v in x] != list(ref_codes)
     assert list(fp8.e4m3_encode(x)) == list(ref_codes)
+
+
+# ------------------------------------------------------------------ mutants of the per-token projections
+
+def _project_variant(kind):
+    """ref.project_tiny with one plausible slip planted in its output."""
+    def project(h, w, n_h, d_h, d_r, base=10000.0):
+        c, k_r, q_c, q_r = ref.project_tiny(h, w, n_h, d_h, d_r, base)
+        L = h.shape[0]
+        pos = np.arange(L)
+        raw_k = h @ np.asarray(w["kr"]).T
+        raw_q = (h @ np.asarray(w["qr"]).T).reshape(L, n_h, d_r)
+        if kind == "k_rope_at_0":
+            k_r = raw_k
+        elif kind == "q_rope_at_0":
+            q_r = raw_q
+        elif kind == "q_rope_at_t_minus_1":
+            q_r = ref.rope(raw_q, (pos - 1)[:, None], base)
+        elif kind == "k_rope_at_j_plus_1":
+            k_r = ref.rope(raw_k, pos + 1, base)
+        elif kind == "c_of_next_token":
+            c = np.roll(c, -1, axis=0)
+        elif kind == "w_dkv_transposed":
+            c = h @ np.asarray(w["dkv"])
+        elif kind == "k_rope_from_first_query_head":
+            k_r = ref.rope(raw_q[:, 0, :], pos, base)
+        return c, k_r, q_c, q_r
+    return project
+
+
+PROJECTION_MUTANTS = ("k_rope_at_0", "q_rope_at_0", "q_rope_at_t_minus_1", "k_rope_at_j_plus_1",
+                      "c_of_next_token", "w_dkv_transposed", "k_rope_from_first_query_head")
+
+
+@pytest.mark.parametrize("kind", PROJECTION_MUTANTS)
+def test_projection_mutant_is_caught(kind):
+    from test_oracle_projections import TOL, projection_errors
+    layer = workloads.tiny_layer(seed=1)
+    err = projection_errors(_project_variant(kind), layer, positions=[0, 1, 64, 127])
+    assert any(v > TOL for v in err.values()), f"projection mutant {kind} passed: {err}"
+    good = projection_errors(ref.project_tiny, layer, positions=[0, 1, 64, 127])
+    assert all(v <= TOL for v in good.values()), good
