@@ -216,6 +216,18 @@ def algorithmic(x):
                 total_flops=attn_flops + up_flops)
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(x, budget_s=12.0):
     """The float64 oracle on host cores over a bounded sample of the same workload: whole
     sequences in batch order (repeating the batch if it is short) until about budget_s
@@ -260,6 +272,7 @@ def cpu_baseline(x, budget_s=12.0):
                 break
         passes += 1
     return {"value": done_tokens / spent, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{seqs} sequences of {x.batch} in batch order ({done_tokens} cached tokens, s_q={x.s_q}, "
                       f"{passes} pass(es) over the batch), float64 NumPy absorbed-form oracle, {spent:.1f} s"}
 
@@ -400,6 +413,9 @@ def main():
         hip.hipEventDestroy(e[7])
     attn_call_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     comb_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    # Distribution of the whole step (stream events around the two calls, dispatch included).
+    step_us = sorted(e[0].elapsed_time(e[3]) * 1e3 for e in evs)
+    pct = lambda q: step_us[min(len(step_us) - 1, int(round(q * (len(step_us) - 1))))]
     print(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step; with events: attention kernel "
           f"{attn_ms * 1e3:.1f} us (append + attention call incl. dispatch {attn_call_ms * 1e3:.1f} us), "
           f"combine {comb_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
@@ -437,6 +453,9 @@ def main():
                    "num_splits": G, "step": "append + partial attention (one call, mla_decode_fwd_append) + "
                                             "combine/up-projection (mla_decode_splitkv_combine)",
                    "warmup_steps_run": n_warm,
+                   "step_us_events": {"p10": round(pct(0.1), 2), "median": round(pct(0.5), 2),
+                                      "p90": round(pct(0.9), 2), "attention_kernel_mean": round(attn_ms * 1e3, 2),
+                                      "combine_call_mean": round(comb_ms * 1e3, 2)},
                    "hbm_gbs_whole_step": round(alg["total_bytes"] / (ms_step * 1e-3) / 1e9, 1)},
         "roofline": roof,
     }

@@ -30,8 +30,19 @@
  *  - Status codes, never exceptions or aborts, cross the ABI.
  *  - Arrays are dense row-major with the shapes given; "elements" are of the
  *    array's own dtype.
- *  - The library keeps no state besides cached device attributes; calls on
- *    different streams may overlap if their outputs and workspaces are disjoint.
+ *  - The library keeps two kinds of state: cached device attributes (per device,
+ *    read once) and one per-thread measurement setting, the events that
+ *    mla_set_attention_events() asks the partial-attention launches of the calling
+ *    thread to record (none unless a caller sets them).  Nothing else persists
+ *    between calls; calls on different streams may overlap if their outputs and
+ *    workspaces are disjoint.
+ *  - Sizes of the pool are given, not bounds on the lengths: the params carry
+ *    num_pages (pool pages, to reject page ids) and max_pages_per_seq (row stride of
+ *    the block table); there is no max_seq_len field, since every kernel reads the
+ *    lengths from seq_lens on the device and clamps them to max_pages_per_seq * P.
+ *  - num_splits counts shares of the whole batch's tokens (the split rule below),
+ *    not splits per sequence: one call launches num_splits workgroups per group of
+ *    query rows, however the lengths are spread over the batch.
  */
 #ifndef MLA_DECODE_H_
 #define MLA_DECODE_H_

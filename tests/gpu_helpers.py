@@ -2,6 +2,7 @@
 through its C ABI, and compute the oracle on the same inputs (or a sample of them).
 Expected values come only from oracle/ on the generator's inputs."""
 import math
+import os
 
 import numpy as np
 import torch
@@ -128,11 +129,30 @@ def to_np(t):
     return t.float().cpu().numpy() if t is not None else None
 
 
+def record(what, rel, mab, lse_err=None, n=None):
+    """Print the achieved error of one comparison and, if MLA_PARITY_LOG names a file, append
+    it there (one line per comparison), so that the margins to the tolerances are visible."""
+    line = f"[parity] {what}: rel_l2={rel:.3e} max_abs={mab:.3e}"
+    if lse_err is not None:
+        line += f" lse_max_err={lse_err:.3e}"
+    if n is not None:
+        line += f" outputs={n}"
+    print(line, flush=True)
+    path = os.environ.get("MLA_PARITY_LOG")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(line + "\n")
+
+
 def compare_sampled(case, out, lse, batches, tol, lse_tol=None, what=""):
+    """Every output of the sequences in `batches` against the oracle: per sequence within `tol`,
+    and the whole set's rel-L2 / max-abs / lse error recorded."""
+    batches = list(batches)
     o_ref, lse_ref = case.oracle(batches)
     got = to_np(out)
     got_lse = to_np(lse)
     res = []
+    lse_worst = 0.0
     for b in batches:
         r = assert_close(got[b], o_ref[b], tol, f"{what} b={b}")
         fin = np.isfinite(lse_ref[b])
@@ -141,5 +161,8 @@ def compare_sampled(case, out, lse, batches, tol, lse_tol=None, what=""):
             lt = lse_tol if lse_tol is not None else tol["max_abs"]
             err = np.max(np.abs(got_lse[b][fin] - lse_ref[b][fin]))
             assert err <= lt, f"{what} b={b}: lse max err {err:.3e}"
+            lse_worst = max(lse_worst, float(err))
         res.append(r)
+    rel, mab = errors(got[batches], o_ref[batches])
+    record(what, rel, mab, lse_worst, n=int(got[batches].size))
     return res
