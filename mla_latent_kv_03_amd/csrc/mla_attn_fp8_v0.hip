@@ -116,7 +116,8 @@ __global__ __launch_bounds__(kMaxThreads) void attn_partial_mfma(const AttnParam
 #pragma unroll
     for (int cb = 0; cb < kCb; ++cb) U[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY;
-    float l_run = 0.f;
+    float l_run = 0.f;     // running sum of the unrounded numerators (for lse)
+    float l_eff = 0.f;     // E4M3: running sum of the rounded weights over their scales (divides U)
 
     auto tile_page = [&](int it) -> int { return pw.get((t0 + it * kT) / p.page_size); };
 
@@ -213,17 +214,11 @@ __global__ __launch_bounds__(kMaxThreads) void attn_partial_mfma(const AttnParam
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = exp2_fast(m_run - m_use);
       float pr[8];
-      float psum = 0.f;
+      float psum = 0.f, esum = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         pr[k] = exp2_fast(x[k] - m_use);
         psum += pr[k];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int cb = 0; cb < kCb; ++cb) U[cb] *= alpha;
       }
       if (FP8) {
 #pragma unroll
@@ -236,6 +231,23 @@ __global__ __launch_bounds__(kMaxThreads) void attn_partial_mfma(const AttnParam
         t = pack_bf16(pr[2], pr[3]); pf[2] = t[0]; pf[3] = t[1];
         t = pack_bf16(pr[4], pr[5]); pf[4] = t[0]; pf[5] = t[1];
         t = pack_bf16(pr[6], pr[7]); pf[6] = t[0]; pf[7] = t[1];
+      }
+      if (FP8) {
+        // U is divided by the sum of the weights that reach the accumulation (the bf16
+        // rounding of p * scale) over the tokens' scales, so numerator and denominator
+        // agree; the lse keeps the sum of the unrounded numerators.
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float r = fminf(__builtin_amdgcn_rcpf(sm.kvs[buf & 1][(k >> 2) * 16 + 4 * g + (k & 3)]), 3.0e38f);
+          esum = __builtin_fmaf((float)pf[k], r, esum);
+        }
+      }
+      l_run = l_run * alpha + psum;
+      l_eff = l_eff * alpha + (FP8 ? esum : psum);
+      m_run = m_new;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int cb = 0; cb < kCb; ++cb) U[cb] *= alpha;
       }
 
       // U^T[cols, heads] += V^T[cols, tokens] P^T[tokens, heads].
@@ -263,7 +275,9 @@ __global__ __launch_bounds__(kMaxThreads) void attn_partial_mfma(const AttnParam
     // Split epilogue: normalized u and the piece's log-sum-exp (natural log).
     float l_tot = l_run + shfl_xor_f(l_run, 16);
     l_tot += shfl_xor_f(l_tot, 32);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float l_div = l_eff + shfl_xor_f(l_eff, 16);
+    l_div += shfl_xor_f(l_div, 32);
+    const float inv = l_div > 0.f ? 1.f / l_div : 0.f;
     const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     const size_t orow = ((size_t)slot * p.s_q + q_pos) * p.n_h + head0 + l16;
     if (g == 0) p.part_lse[orow] = lse;

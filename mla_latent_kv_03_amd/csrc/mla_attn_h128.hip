@@ -468,7 +468,8 @@ void attn_partial_h128(const AttnParams p) {
     f32x16 acc[16];   // U^T block (column block 4 wave + a / 4, head block a % 4)
     float m_ref = -INFINITY;       // this lane's head's reference maximum (base 2)
     float x_max = -INFINITY;       // largest log2 score above m_ref among this lane's tokens
-    float l_part = 0.f;
+    float l_part = 0.f;            // sum of the unrounded numerators (for lse)
+    float l_eff = 0.f;             // E4M3: sum of the rounded weights over their scales (divides U)
 
     // One pass over the piece.  The accumulation of tile it-1 runs in every iteration;
     // before the first tile it uses zero probabilities (and reads a ring slot that holds
@@ -480,6 +481,7 @@ void attn_partial_h128(const AttnParams p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[a][v] = 0.f;
       l_part = 0.f;
+      l_eff = 0.f;
       x_max = -INFINITY;
       if (first_pass && first_piece) {
         // The query copies made at kernel entry must land before the ring and the
@@ -698,13 +700,12 @@ void attn_partial_h128(const AttnParams p) {
         for (int v = 0; v < 16; ++v) x[v] = __builtin_fmaf(s[v], p.scale_log2, nm);
 #pragma unroll
         for (int v = 0; v < 16; v += 2) x_max = fmaxf(x_max, fmaxf(x[v], x[v + 1]));
-        float psum = 0.f;
+        float psum = 0.f, esum = 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           x[v] = exp2_fast(x[v]);
           psum += x[v];
         }
-        l_part += psum;
         if constexpr (FP8) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) x[v] *= tsc[v >> 2][v & 3];
@@ -722,7 +723,25 @@ void attn_partial_h128(const AttnParams p) {
             pf[j + 1] = t[1];
           }
           *(bf16x8*)(pout + half * 1024) = pf;
+          if constexpr (FP8) {
+            // E4M3: the weight that reaches the accumulation is the bf16 rounding w~ of
+            // p * scale, so U is divided by the sum of w~ / scale over the same tokens.
+            // Numerator and denominator then agree, and the rounding only perturbs each
+            // token's weight by its relative rounding error, as with a bf16 cache; dividing
+            // by the sum of the unrounded p instead would scale the whole row by the
+            // rounding error of one token's scale when that token dominates.  The lse keeps
+            // the unrounded sum (it weights this piece against the others).  A token whose
+            // scale is 0 (a tile with no valid page) has w~ = 0.
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float sc = tsc[(8 * half + j) >> 2][j & 3];
+              const float r = fminf(__builtin_amdgcn_rcpf(sc), 3.0e38f);
+              esum = __builtin_fmaf((float)pf[j], r, esum);
+            }
+          }
         }
+        l_part += psum;
+        l_eff += FP8 ? esum : psum;
 #pragma unroll
         for (int a = 16; a < kPv; ++a) acc[a - 16] = mfma32(va[(a - 16) / 4], pb[1][a % 4], acc[a - 16]);
         // Interleave: one accumulation MFMA, then a share of the softmax.
@@ -760,8 +779,9 @@ void attn_partial_h128(const AttnParams p) {
     // barriers from here on wait for LDS operations only, never for the stores.
     const int el = (int)lane_id_opaque(), l32 = el & 31, h = el >> 5;
     const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
+    const float l_div = FP8 ? l_eff + __shfl_xor(l_eff, 32, 64) : l_tot;
     if (h == 0) {
-      sm.l[32 * wave + l32] = l_tot;
+      sm.l[32 * wave + l32] = l_div;
       p.part_lse[row_base + 32 * wave + l32] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
     lds_barrier();
