@@ -70,7 +70,8 @@ typedef enum {
   MLA_ERR_DTYPE = 3,       /* an unsupported dtype combination */
   MLA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than mla_decode_workspace_size() */
   MLA_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
-  MLA_ERR_UNSUPPORTED = 6  /* no kernel for this device */
+  MLA_ERR_UNSUPPORTED = 6, /* no kernel for this device */
+  MLA_ERR_TOO_LARGE = 7    /* mla_decode_fwd_noalloc: the call needs more than its static workspace */
 } mla_status_t;
 
 /*
@@ -220,6 +221,28 @@ mla_status_t mla_decode_fwd_append(const mla_decode_params_t* params, const void
  * the append or combine kernels.  Always returns MLA_OK.
  */
 mla_status_t mla_set_attention_events(void* start, void* stop);
+
+/*
+ * mla_decode_fwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and validation as mla_decode_fwd, except:
+ *  - the workspace is a static device array inside the library, one per device, of
+ *    mla_decode_noalloc_capacity() bytes (64 MiB), set up on the first call on each
+ *    device and kept until the process ends; the call allocates and frees nothing;
+ *  - a call whose workspace (mla_decode_workspace_size) would exceed that size returns
+ *    MLA_ERR_TOO_LARGE and enqueues nothing;
+ *  - out must not be NULL (the partials stay in the library's array);
+ *  - every call on one device shares that device's array, which keeps the last call's
+ *    contents: calls that overlap on one device (e.g. on two streams) race and must be
+ *    ordered by the caller.  No part of the array needs to start at zero.
+ */
+mla_status_t mla_decode_fwd_noalloc(const mla_decode_params_t* params, const void* q_nope, const void* q_pe,
+                                    const void* c_kv, const void* k_pe, const float* kv_scale,
+                                    const int32_t* block_table, const int32_t* seq_lens, const void* w_uv,
+                                    void* out, float* lse, void* stream);
+
+/* Bytes of the static workspace of mla_decode_fwd_noalloc (per device). */
+size_t mla_decode_noalloc_capacity(void);
 
 /* Static description of a status code. */
 const char* mla_status_string(mla_status_t status);

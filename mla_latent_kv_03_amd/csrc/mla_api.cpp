@@ -8,6 +8,7 @@
 
 #include <atomic>
 #include <climits>
+#include <mutex>
 
 #include "mla_kernels.h"
 
@@ -247,6 +248,32 @@ mla_status_t prepare_append(const mla_decode_params_t* params, const void* c_new
   return MLA_OK;
 }
 
+// Workspace of mla_decode_fwd_noalloc: one array per device, in the code object's
+// zero-initialized device memory, held until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the symbol): its
+// device address is looked up once per device, with that device current, and kept.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array, or nullptr if the runtime cannot give it.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();   // leave no sticky error for the caller's next HIP call
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 namespace mla {
@@ -276,6 +303,9 @@ const char* mla_status_string(mla_status_t s) {
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: the HIP runtime reported an error";
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: no kernel for this device";
+    case MLA_ERR_TOO_LARGE:
+      return "MLA_ERR_TOO_LARGE: the call needs more workspace than the library's static buffer "
+             "(mla_decode_noalloc_capacity() bytes) holds";
   }
   return "unknown mla_status_t";
 }
@@ -302,6 +332,26 @@ mla_status_t mla_decode_fwd(const mla_decode_params_t* params, const void* q_nop
                                       workspace, workspace_bytes, a, G);
   if (st != MLA_OK) return st;
   return launch_fwd(*params, a, G, w_uv, out, lse, workspace, (hipStream_t)stream);
+}
+
+size_t mla_decode_noalloc_capacity(void) { return kScratchBytes; }
+
+mla_status_t mla_decode_fwd_noalloc(const mla_decode_params_t* params, const void* q_nope, const void* q_pe,
+                                    const void* c_kv, const void* k_pe, const float* kv_scale,
+                                    const int32_t* block_table, const int32_t* seq_lens, const void* w_uv,
+                                    void* out, float* lse, void* stream) {
+  const mla_status_t st = check_common(params);
+  if (st != MLA_OK) return st;
+  if (!out) return MLA_ERR_NULL;
+  const int G = resolve_splits(*params);
+  if (G <= 0) return MLA_ERR_UNSUPPORTED;
+  if (layout_of(*params, G).total > kScratchBytes) return MLA_ERR_TOO_LARGE;
+  void* ws = scratch_address();
+  if (!ws) return MLA_ERR_HIP;
+  // Nothing in the scratch array has to start at zero: the partial-attention launch writes
+  // the split table and every partial that the combine then reads.
+  return mla_decode_fwd(params, q_nope, q_pe, c_kv, k_pe, kv_scale, block_table, seq_lens, w_uv, out, lse, ws,
+                        kScratchBytes, stream);
 }
 
 mla_status_t mla_decode_fwd_append(const mla_decode_params_t* params, const void* c_new, const void* k_pe_new,

@@ -127,3 +127,21 @@ def test_fp32_path_limits(b):
     assert fwd(b, p) == 2
     p = v3(b, q_dtype=b.F32, kv_dtype=b.F32, d_c=64, d_r=16, d_v=16, n_h=8)
     assert fwd(b, p, ws_bytes=0) == 4
+
+
+def test_noalloc_entry_point_validation(b):
+    """mla_decode_fwd_noalloc checks everything on the host before it touches its static
+    workspace: a call that needs more than the capacity is rejected, so is out == NULL."""
+    lib = b.LIB
+    cap = lib.mla_decode_noalloc_capacity()
+    assert cap == 64 << 20
+    call = lambda p, out=FAKE: lib.mla_decode_fwd_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                                         FAKE, out, None, None)
+    small = v3(b, batch=4, num_splits=16)
+    assert b.mla_decode_workspace_size(small) <= cap
+    assert call(small, out=None) == 1
+    big = v3(b, batch=512, num_splits=256)                    # (256 + 512) slots x 128 heads x 1 KiB > 64 MiB
+    assert b.mla_decode_workspace_size(big) > cap
+    assert call(big) == 7
+    assert b.lib_status_string(7).startswith("MLA_ERR_TOO_LARGE")
+    assert call(v3(b, d_c=256)) == 2
