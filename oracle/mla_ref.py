@@ -34,6 +34,16 @@ Pins (each function is checked by something other than itself, see tests/):
                      (complex exponentials at the token's own position) and every score
                      term q^R_{t,i} . k^R_j from the unrotated projections
                      (tests/test_oracle_projections.py; planted mutants caught).
+  cache_rows,
+  query_rows,
+  output_projection,
+  fold_output_weights
+                     scalar loops with complex-exponential rotations at arbitrary
+                     positions; equality with project_tiny / absorb_query on the tiny
+                     layer; the explicit products W^QK_i = (W^UK_i)^T W^Q_i and
+                     W^O_i W^UV_i against the factored forms; the folded output path
+                     against plain multi-head attention followed by W^O
+                     (tests/test_oracle_adjacent.py; planted mutants caught).
   mla_nonabsorbed    absorbed == non-absorbed identity; pure-Python brute force.
   mla_absorbed       torch SDPA in float64; brute force; closed forms.
   split_partial,
@@ -110,6 +120,63 @@ def absorb_query(q_c, w_uk):
     q_c = np.asarray(q_c, np.float64)
     w_uk = np.asarray(w_uk, np.float64)
     return np.stack([w_uk[i].T @ q_c[i] for i in range(q_c.shape[0])])
+
+
+def cache_rows(h, w_dkv, w_kr, positions, base=10000.0):
+    """The cache row of new tokens with hidden states h [..., d] at absolute positions [...].
+
+    [DC] latent equation: c_t = W^DKV h_t.  [DC] "Decoupled RoPE": k^R_t = RoPE(W^KR h_t),
+    rotated at the token's own position (reading R5: cached after rotation).
+    w_dkv [d_c, d], w_kr [d_r, d].  Returns (c [..., d_c], k_r [..., d_r]) in float64.
+    """
+    h = np.asarray(h, np.float64)
+    c = h @ np.asarray(w_dkv, np.float64).T
+    k_r = rope(h @ np.asarray(w_kr, np.float64).T, positions, base)
+    return c, k_r
+
+
+def query_rows(h, w_q, w_uk, w_qr, positions, base=10000.0):
+    """Absorbed and RoPE queries of new tokens with hidden states h [..., d].
+
+    [DC] score-side equation: head i's absorbed query is W^QK_i h_t with
+    W^QK_i = (W^UK_i)^T W^Q_i (reading R1: the key up-projection is W^UK_i); by
+    associativity it is formed here as (W^UK_i)^T (W^Q_i h_t).  [DC] "Decoupled RoPE":
+    q^R_i = RoPE(W^QR_i h_t) at the token's position.
+    w_q [n_h*d_h, d] (rows of head i at i*d_h), w_uk [n_h, d_h, d_c], w_qr [n_h*d_r, d].
+    Returns q_nope [..., n_h, d_c] and q_pe [..., n_h, d_r].
+    """
+    h = np.asarray(h, np.float64)
+    w_uk = np.asarray(w_uk, np.float64)
+    n_h, d_h, _ = w_uk.shape
+    lead = h.shape[:-1]
+    q_c = (h @ np.asarray(w_q, np.float64).T).reshape(lead + (n_h, d_h))
+    q_nope = np.einsum("...ik,ikc->...ic", q_c, w_uk)
+    w_qr = np.asarray(w_qr, np.float64)
+    d_r = w_qr.shape[0] // n_h
+    raw = (h @ w_qr.T).reshape(lead + (n_h, d_r))
+    q_pe = rope(raw, np.asarray(positions, np.float64)[..., None], base)
+    return q_nope, q_pe
+
+
+def output_projection(o, w_o):
+    """y = sum_i W^O_i o_i: the heads' outputs through the output projection.
+
+    [AA] section 5 (the per-head outputs W^UV_i u_i feed W^O; W^UV can be folded into it).
+    o [..., n_h, d_v]; w_o [d, n_h*d_v] whose column block i (columns i*d_v ..) is W^O_i.
+    Returns y [..., d].
+    """
+    o = np.asarray(o, np.float64)
+    lead = o.shape[:-2]
+    return o.reshape(lead + (-1,)) @ np.asarray(w_o, np.float64).T
+
+
+def fold_output_weights(w_o, w_uv):
+    """W^OV with column block i = W^O_i W^UV_i, shape [d, n_h*d_c]: the output-side fold
+    ([AA] section 5: W^UV folds into W^O offline), so that y = sum_i W^OV_i u_i."""
+    w_o = np.asarray(w_o, np.float64)
+    w_uv = np.asarray(w_uv, np.float64)
+    n_h, d_v, _ = w_uv.shape
+    return np.concatenate([w_o[:, i * d_v:(i + 1) * d_v] @ w_uv[i] for i in range(n_h)], axis=1)
 
 
 # ----------------------------------------------------------------------------
