@@ -163,6 +163,9 @@ mla_status_t mla_decode_fwd(const mla_decode_params_t* params, const void* q_nop
  *   u   = sum_s exp(lse_s - lse) u_s,   o = W^UV_i u.
  * Reads split_table, partial_lse and partial_u from `workspace` (layout above),
  * e.g. as left by mla_decode_fwd with out == NULL, or written by the caller.
+ * w_uv may be NULL: then out receives the merged latents u as float32
+ * [B, s_q, n_h, d_c] instead of o (the input of mla_output_projection with folded
+ * weights).
  * Slot ranges are clipped to [0, G + B); a sequence whose slots are all empty
  * yields o = 0 and lse = -inf.
  */
@@ -221,6 +224,94 @@ mla_status_t mla_decode_fwd_append(const mla_decode_params_t* params, const void
  * the append or combine kernels.  Always returns MLA_OK.
  */
 mla_status_t mla_set_attention_events(void* start, void* stop);
+
+/*
+ * ----------------------------------------------------------------------------------
+ * Projections adjacent to the decode step (page "MLA deep compression": low-rank
+ * projection, absorption and decoupled-RoPE sections; "Attention-head anatomy",
+ * section 5: W^UK folds into the query path, W^UV into W^O).  Operands are dense
+ * row-major; every product contracts over the last (contiguous) index of both operands.
+ * bf16 operands (params->q_dtype / w_dtype == BF16) run on MFMAs with float32
+ * accumulation and need the contraction width a multiple of 32, the other product
+ * widths multiples of 16 and 16-byte aligned operand pointers; float32 operands accept
+ * any size.  RoPE rotates interleaved pairs (x[2m], x[2m+1]) at position p by the angle
+ * p * rope_base^(-2m/d_r), taken in float64.  Each call needs a workspace of the size
+ * its *_workspace_size function returns (0 means invalid params); a workspace too small
+ * gives MLA_ERR_WORKSPACE.  None of them reads seq_lens.
+ * ----------------------------------------------------------------------------------
+ */
+
+/*
+ * Cache write: the new tokens' cache rows from their hidden states, written into the
+ * paged pool (the step that precedes attention):
+ *     c_t = W^DKV h_t,   k^R_t = RoPE(W^KR h_t, positions[t]),   pool row = [c_t | k^R_t]
+ *  h          [B, s_new, d_model]  q_dtype (BF16 or F32)
+ *  w_dkv      [d_c, d_model]       q_dtype
+ *  w_kr       [d_r, d_model]       q_dtype
+ *  positions  [B, s_new] int32: absolute token index, the RoPE position and the slot
+ *             (same slot rule and skips as mla_paged_cache_append)
+ *  c_kv, k_pe, kv_scale, block_table: the pool, as in mla_paged_cache_append.
+ * The row is computed in float32 and stored per params->kv_dtype: BF16 (round to
+ * nearest even; needs q_dtype BF16), F32 (needs q_dtype F32), or FP8_E4M3 with the
+ * per-token scale of mla_paged_cache_append's quantizer applied to the float32 row.
+ * Uses params batch, d_c, d_r (both even, d_c + d_r <= 1280), page_size, num_pages,
+ * max_pages_per_seq, strides, q_dtype and kv_dtype.
+ */
+size_t mla_cache_write_workspace_size(const mla_decode_params_t* params, int32_t d_model, int32_t s_new);
+mla_status_t mla_cache_write(const mla_decode_params_t* params, int32_t d_model, int32_t s_new, const void* h,
+                             const void* w_dkv, const void* w_kr, const int32_t* positions, float rope_base,
+                             const int32_t* block_table, void* c_kv, void* k_pe, float* kv_scale, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * Query prologue: the decode call's queries from the new tokens' hidden states,
+ *     q_nope[.., i, :] = (W^UK_i)^T (W^Q_i h_t)      (= W^QK_i h_t of the score-side
+ *                                                     equation, formed in two products)
+ *     q_pe[.., i, :]   = RoPE(W^QR_i h_t, positions[t])
+ *  h        [B, s_q, d_model]      q_dtype (BF16 or F32)
+ *  w_q      [n_h * d_h, d_model]   rows i*d_h .. are W^Q_i
+ *  w_uk_t   [n_h, d_c, d_h]        head i's (W^UK_i)^T (the up-projection transposed)
+ *  w_qr     [n_h * d_r, d_model]   rows i*d_r .. are W^QR_i
+ *  positions [B, s_q] int32
+ *  q_nope   [B, s_q, n_h, d_c], q_pe [B, s_q, n_h, d_r]   q_dtype (the inputs of
+ *           mla_decode_fwd)
+ * W^Q_i h is kept in float32 and enters the second product as a bf16 high part plus
+ * remainder.  Uses params batch, s_q, n_h, d_c, d_r and q_dtype.
+ */
+size_t mla_query_prologue_workspace_size(const mla_decode_params_t* params, int32_t d_model, int32_t d_h);
+mla_status_t mla_query_prologue(const mla_decode_params_t* params, int32_t d_model, int32_t d_h, const void* h,
+                                const void* w_q, const void* w_uk_t, const void* w_qr, const int32_t* positions,
+                                float rope_base, void* q_nope, void* q_pe, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * Output projection y = W x of the B * s_q rows of x:
+ *   unfolded  x = the decode output o [B, s_q, n_h, d_v] (width = n_h * d_v), W = W^O
+ *             [d_model, n_h * d_v] (column block i is W^O_i): y = sum_i W^O_i W^UV_i u_i;
+ *   folded    x = the merged latents u [B, s_q, n_h, d_c] (float32, from
+ *             mla_decode_splitkv_combine with w_uv = NULL; width = n_h * d_c), W = W^OV
+ *             from mla_fold_output_weights: the same y.
+ *  x_dtype    BF16 or F32 (F32 enters bf16 products as high part plus remainder)
+ *  w          [d_model, width]  params->w_dtype
+ *  y          [B, s_q, d_model] params->out_dtype
+ */
+size_t mla_output_projection_workspace_size(const mla_decode_params_t* params, int32_t d_model, int32_t width,
+                                            mla_dtype_t x_dtype);
+mla_status_t mla_output_projection(const mla_decode_params_t* params, int32_t d_model, int32_t width,
+                                   mla_dtype_t x_dtype, const void* x, const void* w, void* y, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * Offline fold of W^UV into W^O: w_ov [d_model, n_h * d_c] with column block i =
+ * W^O_i W^UV_i ([d_model, d_v] x [d_v, d_c]), in params->w_dtype (bf16: float32
+ * accumulation, one rounding).  w_o [d_model, n_h * d_v], w_uv [n_h, d_v, d_c].  The
+ * folded weights hold d_c / d_v times the bytes of W^O (4x at the V3 shape), so at decode
+ * the unfolded projection reads less; the fold is the page's offline form.
+ */
+size_t mla_fold_output_weights_workspace_size(const mla_decode_params_t* params);
+mla_status_t mla_fold_output_weights(const mla_decode_params_t* params, int32_t d_model, const void* w_o,
+                                     const void* w_uv, void* w_ov, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /*
  * mla_decode_fwd without a workspace argument, for callers that cannot allocate device

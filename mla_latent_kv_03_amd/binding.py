@@ -20,7 +20,10 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE"
           5: "MLA_ERR_HIP", 6: "MLA_ERR_UNSUPPORTED", 7: "MLA_ERR_TOO_LARGE"}
 EXPORTS = ("mla_decode_num_splits", "mla_decode_workspace_size", "mla_decode_fwd", "mla_decode_splitkv_combine",
            "mla_paged_cache_append", "mla_decode_fwd_append", "mla_set_attention_events", "mla_status_string",
-           "mla_abi_version", "mla_decode_fwd_noalloc", "mla_decode_noalloc_capacity")
+           "mla_abi_version", "mla_decode_fwd_noalloc", "mla_decode_noalloc_capacity", "mla_cache_write",
+           "mla_cache_write_workspace_size", "mla_query_prologue", "mla_query_prologue_workspace_size",
+           "mla_output_projection", "mla_output_projection_workspace_size", "mla_fold_output_weights",
+           "mla_fold_output_weights_workspace_size")
 
 
 class DecodeParams(ctypes.Structure):
@@ -67,6 +70,23 @@ def _load():
     lib.mla_decode_fwd_noalloc.restype = ctypes.c_int
     lib.mla_decode_noalloc_capacity.argtypes = []
     lib.mla_decode_noalloc_capacity.restype = ctypes.c_size_t
+    i32, f32, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.mla_cache_write_workspace_size.argtypes = [P, i32, i32]
+    lib.mla_cache_write_workspace_size.restype = sz
+    lib.mla_cache_write.argtypes = [P, i32, i32, vp, vp, vp, i32p, f32, i32p, vp, vp, f32p, vp, sz, vp]
+    lib.mla_cache_write.restype = ctypes.c_int
+    lib.mla_query_prologue_workspace_size.argtypes = [P, i32, i32]
+    lib.mla_query_prologue_workspace_size.restype = sz
+    lib.mla_query_prologue.argtypes = [P, i32, i32, vp, vp, vp, vp, i32p, f32, vp, vp, vp, sz, vp]
+    lib.mla_query_prologue.restype = ctypes.c_int
+    lib.mla_output_projection_workspace_size.argtypes = [P, i32, i32, ctypes.c_int]
+    lib.mla_output_projection_workspace_size.restype = sz
+    lib.mla_output_projection.argtypes = [P, i32, i32, ctypes.c_int, vp, vp, vp, vp, sz, vp]
+    lib.mla_output_projection.restype = ctypes.c_int
+    lib.mla_fold_output_weights_workspace_size.argtypes = [P]
+    lib.mla_fold_output_weights_workspace_size.restype = sz
+    lib.mla_fold_output_weights.argtypes = [P, i32, vp, vp, vp, vp, sz, vp]
+    lib.mla_fold_output_weights.restype = ctypes.c_int
     lib.mla_set_attention_events.argtypes = [vp, vp]
     lib.mla_set_attention_events.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -226,6 +246,76 @@ def mla_paged_cache_append(params, c_new, k_pe_new, positions, block_table, c_kv
                                       _DTYPE_CODE[c_new.dtype], _ptr(positions), _ptr(block_table), _ptr(c_kv),
                                       _ptr(k_pe), _ptr(kv_scale), _stream())
     _check(code, "mla_paged_cache_append")
+
+
+def _workspace(nbytes, where, device):
+    if nbytes == 0:
+        raise MLAError(2, where)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def mla_cache_write(params, h, w_dkv, w_kr, positions, block_table, c_kv, k_pe, kv_scale=None, *, rope_base=10000.0,
+                    workspace=None):
+    """Cache rows of new tokens from their hidden states h [B, s_new, d_model], written into the pool views."""
+    B, s_new, d_model = h.shape
+    if workspace is None:
+        workspace = _workspace(LIB.mla_cache_write_workspace_size(ctypes.byref(params), d_model, s_new),
+                               "mla_cache_write_workspace_size", h.device)
+    code = LIB.mla_cache_write(ctypes.byref(params), int(d_model), int(s_new), _ptr(h), _ptr(w_dkv), _ptr(w_kr),
+                               _ptr(positions), float(rope_base), _ptr(block_table), _ptr(c_kv), _ptr(k_pe),
+                               _ptr(kv_scale), _ptr(workspace), workspace.numel(), _stream())
+    _check(code, "mla_cache_write")
+    return workspace
+
+
+def mla_query_prologue(params, h, w_q, w_uk_t, w_qr, positions, q_nope=None, q_pe=None, *, d_h, rope_base=10000.0,
+                       workspace=None):
+    """q_nope [B, s_q, n_h, d_c] and q_pe [B, s_q, n_h, d_r] from hidden states h [B, s_q, d_model]."""
+    B, s_q, d_model = h.shape
+    dt = h.dtype
+    if q_nope is None:
+        q_nope = torch.empty(B, s_q, params.n_h, params.d_c, dtype=dt, device=h.device)
+    if q_pe is None:
+        q_pe = torch.empty(B, s_q, params.n_h, params.d_r, dtype=dt, device=h.device)
+    if workspace is None:
+        workspace = _workspace(LIB.mla_query_prologue_workspace_size(ctypes.byref(params), d_model, int(d_h)),
+                               "mla_query_prologue_workspace_size", h.device)
+    code = LIB.mla_query_prologue(ctypes.byref(params), int(d_model), int(d_h), _ptr(h), _ptr(w_q), _ptr(w_uk_t),
+                                  _ptr(w_qr), _ptr(positions), float(rope_base), _ptr(q_nope), _ptr(q_pe),
+                                  _ptr(workspace), workspace.numel(), _stream())
+    _check(code, "mla_query_prologue")
+    return q_nope, q_pe
+
+
+def mla_output_projection(params, x, w, y=None, *, workspace=None):
+    """y [B, s_q, d_model] = W x for x [B, s_q, n_h, width_per_head] (o with W^O, or u with W^OV)."""
+    B, s_q = x.shape[:2]
+    width = x[0, 0].numel()
+    d_model = w.shape[0]
+    x_dt = _DTYPE_CODE[x.dtype]
+    if y is None:
+        y = torch.empty(B, s_q, d_model, dtype=torch.bfloat16 if params.out_dtype == BF16 else torch.float32,
+                        device=x.device)
+    if workspace is None:
+        workspace = _workspace(LIB.mla_output_projection_workspace_size(ctypes.byref(params), d_model, width, x_dt),
+                               "mla_output_projection_workspace_size", x.device)
+    code = LIB.mla_output_projection(ctypes.byref(params), int(d_model), int(width), x_dt, _ptr(x), _ptr(w), _ptr(y),
+                                     _ptr(workspace), workspace.numel(), _stream())
+    _check(code, "mla_output_projection")
+    return y
+
+
+def mla_fold_output_weights(params, w_o, w_uv, w_ov=None):
+    """W^OV [d_model, n_h * d_c] with column block i = W^O_i W^UV_i."""
+    d_model = w_o.shape[0]
+    if w_ov is None:
+        w_ov = torch.empty(d_model, params.n_h * params.d_c, dtype=w_o.dtype, device=w_o.device)
+    workspace = _workspace(LIB.mla_fold_output_weights_workspace_size(ctypes.byref(params)),
+                           "mla_fold_output_weights_workspace_size", w_o.device)
+    code = LIB.mla_fold_output_weights(ctypes.byref(params), int(d_model), _ptr(w_o), _ptr(w_uv), _ptr(w_ov),
+                                       _ptr(workspace), workspace.numel(), _stream())
+    _check(code, "mla_fold_output_weights")
+    return w_ov
 
 
 def mla_set_attention_events(start=None, stop=None):

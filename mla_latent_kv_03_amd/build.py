@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["mla_api.cpp", "mla_attn_mfma.hip", "mla_attn_h128.hip", "mla_attn_fp8_v0.hip", "mla_attn_f32.hip", "mla_combine.hip", "mla_append.hip"]
+SOURCES = ["mla_api.cpp", "mla_proj_api.cpp", "mla_attn_mfma.hip", "mla_attn_h128.hip", "mla_attn_fp8_v0.hip",
+           "mla_attn_f32.hip", "mla_combine.hip", "mla_append.hip", "mla_proj.hip"]
 ARCH = "gfx950"
 
 

@@ -391,9 +391,10 @@ mla_status_t mla_decode_splitkv_combine(const mla_decode_params_t* params, const
                                         void* stream) {
   mla_status_t st = check_common(params);
   if (st != MLA_OK) return st;
-  if (!w_uv || !out) return MLA_ERR_NULL;
+  if (!out) return MLA_ERR_NULL;
   const Path path = path_of(*params);
-  if (path != Path::kF32 && (!aligned16(w_uv) || !aligned16(workspace))) return MLA_ERR_SHAPE;
+  if (path != Path::kF32 && ((w_uv && !aligned16(w_uv)) || !aligned16(workspace) || (!w_uv && !aligned16(out))))
+    return MLA_ERR_SHAPE;
   const int G = resolve_splits(*params);
   if (G <= 0) return MLA_ERR_UNSUPPORTED;
   const Layout l = layout_of(*params, G);

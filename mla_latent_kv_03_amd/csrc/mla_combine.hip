@@ -158,6 +158,11 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const 
     return acc;
   };
   auto store_u = [&](int i, int hh, f32x4 a) {
+    if (!p.w_uv) {
+      // No up-projection: the merged latents go out as float32 [B, s_q, n_h, d_c].
+      if (i < nrows) *(f32x4*)((float*)p.out + ((size_t)(row0 + i) * p.n_h + head) * kDc + 256 * hh + 4 * lane) = a;
+      return;
+    }
     bf16x4 hi, lo;
 #pragma unroll
     for (int j = 0; j < 4; j += 2) {
@@ -176,7 +181,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const 
   if (M > 1) start(1, B);
   // W^UV_i rows for phase 2 after the first units' loads, which must not queue behind them.
   bf16x8 bw[kDc / 32];
-  {
+  if (p.w_uv) {
     const bf16* wrow = (const bf16*)p.w_uv + ((size_t)head * kDv + 16 * wave + l16) * kDc + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < kDc / 32; ++kk) bw[kk] = *(const bf16x8*)(wrow + kk * 32);
@@ -202,6 +207,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const 
     }
   }
   __syncthreads();
+  if (!p.w_uv) return;   // kernel-uniform
 
   // O[rows, v] = U[rows, k] W^T[k, v]; lane holds O[row 4g + i][v = 16 wave + l16].
   // Tile rows past the block's last row hold stale values; they only reach outputs
@@ -260,8 +266,10 @@ __global__ __launch_bounds__(256) void combine_upproj_f32(const CombineParams p)
         if (l != -INFINITY) acc = fmaf(expf(l - mx) * inv, ((const float*)p.part_u)[prow * p.d_c + k], acc);
       }
       u_s[rr][k] = acc;
+      if (!p.w_uv) ((float*)p.out)[((size_t)r * p.n_h + head) * p.d_c + k] = acc;
     }
   }
+  if (!p.w_uv) return;   // kernel-uniform: the merged latents were the output
   __syncthreads();
   const float* wh = (const float*)p.w_uv + (size_t)head * p.d_v * p.d_c;
   float* out = (float*)p.out;

@@ -64,6 +64,58 @@ struct AppendParams {
   int32_t mode;              // 0: copy bf16, 1: copy f32, 2: quantize to E4M3 + scale
 };
 
+// C = A B^T for the projections around the decode step (mla_proj.hip).  Element (m, k) of
+// batch t of A is at a + t * a_bs + m * lda + k (B likewise); partial j of C at
+// c + j * c_ks + t * c_bs + m * ldc + n.  K split into chunks of kchunk (a multiple of 32).
+struct GemmArgs {
+  const void* a;
+  const void* b;
+  void* c;                   // float32 partials, or bf16 when out_bf16 (one chunk only)
+  int64_t lda, ldb, ldc;
+  int64_t a_bs, b_bs, c_bs, c_ks;
+  int32_t M, N, K, kchunk, batch;
+  int32_t a_f32;             // bf16 operands: A is float32 (enters as bf16 high + remainder)
+  int32_t out_bf16;
+};
+
+// Cache write finish: sums the partials [ksplit][T][d_c + d_r] of each new token's row,
+// rotates its RoPE part and writes the pool slot.
+struct CacheWriteArgs {
+  const float* part;
+  int64_t part_ks;
+  int32_t ksplit, d_c, d_r, s_new;
+  const int32_t* positions;
+  const int32_t* block_table;
+  void* c_kv;
+  void* k_pe;
+  float* kv_scale;
+  int64_t c_stride, k_stride;
+  int32_t page_size, num_pages, max_pages;
+  int32_t mode;              // 0: bf16 row, 1: float32 row, 2: E4M3 codes + scale
+  float rope_base;
+};
+
+// Query prologue finish: q^C partials -> q_c (float32), q^R partials -> RoPE -> q_pe.
+struct QueryArgs {
+  const float* part_c;
+  const float* part_r;
+  int64_t part_c_ks, part_r_ks;
+  int32_t ksplit, ksplit_r, n_h, d_h, d_r;
+  const int32_t* positions;
+  float* q_c;                // [T][n_h * d_h]
+  void* q_pe;                // [T][n_h * d_r]
+  int32_t out_bf16;
+  float rope_base;
+};
+
+hipError_t launch_gemm_nt(const GemmArgs& g, bool bf16_operands, int ksplit, hipStream_t s);
+hipError_t launch_cache_write_finish(const CacheWriteArgs& a, int tokens, hipStream_t s);
+hipError_t launch_query_finish(const QueryArgs& a, int tokens, hipStream_t s);
+hipError_t launch_sum_partials(const float* part, int64_t part_ks, int ksplit, int64_t n, void* out, bool out_bf16,
+                               hipStream_t s);
+hipError_t launch_transpose_heads(const void* src, void* dst, int heads, int rows, int cols, bool bf16_elems,
+                                  hipStream_t s);
+
 // Heads of one query position handled by one workgroup of the bf16 kernel.
 int attn_heads_per_group(int n_h);
 // Start/stop events for the partial-attention kernel of the calling thread's next

@@ -177,3 +177,21 @@ def v3_long_fp8(seed=5, B=4, L=131072):
     """Batch 4, 131072-token caches to be stored as E4M3 + per-token scale; 64 splits each."""
     return make_decode([L] * B, paged=False, kv_dtype="fp8", seed=seed, softmax_scale=V3_SCALE,
                        name="v3_long_fp8_b4_l131072", **V3)
+
+
+def layer_weights(seed, *, d_model, n_h, d_c, d_h, d_r, d_v, n_tokens, with_o=True):
+    """Hidden states of n_tokens new tokens and the projection weights of one MLA layer, as
+    float32 draws (fixed order: h, W^DKV, W^KR, W^Q, W^UK, W^QR, W^UV, W^O).  h ~ N(0, 1);
+    every weight ~ N(0, 1/fan_in) with fan_in its input width (d_model for the projections of
+    h, d_c for W^UK / W^UV, n_h * d_v for W^O).  Layouts: dkv [d_c, d_model], kr [d_r, d_model],
+    q [n_h*d_h, d_model], uk [n_h, d_h, d_c], qr [n_h*d_r, d_model], uv [n_h, d_v, d_c],
+    o [d_model, n_h*d_v]."""
+    rng = np.random.default_rng(seed)
+    out = {"h": _normal(rng, (n_tokens, d_model))}
+    for name, shape, fan in (("dkv", (d_c, d_model), d_model), ("kr", (d_r, d_model), d_model),
+                             ("q", (n_h * d_h, d_model), d_model), ("uk", (n_h, d_h, d_c), d_c),
+                             ("qr", (n_h * d_r, d_model), d_model), ("uv", (n_h, d_v, d_c), d_c)):
+        out[name] = _normal(rng, shape, 1.0 / math.sqrt(fan))
+    if with_o:
+        out["o"] = _normal(rng, (d_model, n_h * d_v), 1.0 / math.sqrt(n_h * d_v))
+    return out

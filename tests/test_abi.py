@@ -112,7 +112,11 @@ def test_combine_and_append_validation(b):
     p = v3(b)
     lib = b.LIB
     assert lib.mla_decode_splitkv_combine(ctypes.byref(p), FAKE, 10, FAKE, FAKE, None, None) == 4
-    assert lib.mla_decode_splitkv_combine(ctypes.byref(p), FAKE, 1 << 40, None, FAKE, None, None) == 1
+    assert lib.mla_decode_splitkv_combine(ctypes.byref(p), FAKE, 1 << 40, FAKE, None, None, None) == 1
+    assert lib.mla_decode_splitkv_combine(ctypes.byref(p), FAKE, 1 << 40, None, None, None, None) == 1
+    # w_uv = NULL is the merged-latent mode: out must then be 16-byte aligned
+    assert lib.mla_decode_splitkv_combine(ctypes.byref(p), FAKE, 1 << 40, None, ctypes.c_void_p(0x10004), None,
+                                          None) == 2
     ap = lambda params, in_dt, scale=None, s_new=3: lib.mla_paged_cache_append(
         ctypes.byref(params), FAKE, FAKE, s_new, in_dt, FAKE, FAKE, FAKE, FAKE, scale, None)
     assert ap(p, b.F32) == 3                                   # f32 rows into a bf16 cache
@@ -145,3 +149,33 @@ def test_noalloc_entry_point_validation(b):
     assert call(big) == 7
     assert b.lib_status_string(7).startswith("MLA_ERR_TOO_LARGE")
     assert call(v3(b, d_c=256)) == 2
+
+
+def test_projection_entry_points_validation(b):
+    """Host-side checks of the projection entry points (no launch happens on these paths)."""
+    lib = b.LIB
+    p = v3(b, batch=4, s_q=1)
+    # cache write: bf16 inputs with a bf16 pool; d_model must be a multiple of 32 on the bf16 path
+    assert lib.mla_cache_write_workspace_size(ctypes.byref(p), 7168, 1) > 0
+    assert lib.mla_cache_write_workspace_size(ctypes.byref(p), 7000, 1) == 0
+    assert lib.mla_cache_write_workspace_size(ctypes.byref(v3(b, q_dtype=b.F32)), 7168, 1) == 0   # f32 rows, bf16 pool
+    cw = lambda params, ws_bytes=1 << 30, kv_scale=None, base=10000.0: lib.mla_cache_write(
+        ctypes.byref(params), 7168, 1, FAKE, FAKE, FAKE, FAKE, base, FAKE, FAKE, FAKE, kv_scale, FAKE, ws_bytes, None)
+    assert cw(p, ws_bytes=16) == 4
+    assert cw(p, kv_scale=FAKE) == 3
+    assert cw(v3(b, kv_dtype=b.FP8)) == 1
+    assert cw(p, base=0.5) == 2
+    # query prologue: d_h must be a multiple of 32 on the bf16 path
+    assert lib.mla_query_prologue_workspace_size(ctypes.byref(p), 7168, 128) > 0
+    assert lib.mla_query_prologue_workspace_size(ctypes.byref(p), 7168, 48) == 0
+    qp = lambda ws_bytes: lib.mla_query_prologue(ctypes.byref(p), 7168, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 10000.0,
+                                                 FAKE, FAKE, FAKE, ws_bytes, None)
+    assert qp(16) == 4
+    # output projection: float32 weights need float32 x; bf16 weights need width % 32 == 0
+    assert lib.mla_output_projection_workspace_size(ctypes.byref(p), 7168, 16384, b.BF16) > 0
+    assert lib.mla_output_projection_workspace_size(ctypes.byref(p), 7168, 16380, b.BF16) == 0
+    assert lib.mla_output_projection_workspace_size(ctypes.byref(v3(b, q_dtype=b.F32)), 64, 128, b.BF16) == 0
+    assert lib.mla_output_projection(ctypes.byref(p), 7168, 16384, b.BF16, None, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    # fold: bf16 needs d_v % 32 == 0
+    assert lib.mla_fold_output_weights_workspace_size(ctypes.byref(p)) == 128 * 128 * 512 * 2
+    assert lib.mla_fold_output_weights(ctypes.byref(v3(b, d_v=48)), 7168, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2
