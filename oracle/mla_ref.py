@@ -44,6 +44,12 @@ Pins (each function is checked by something other than itself, see tests/):
                      W^O_i W^UV_i against the factored forms; the folded output path
                      against plain multi-head attention followed by W^O
                      (tests/test_oracle_adjacent.py; planted mutants caught).
+  gqla_expand,
+  gqla_decode        the GQLA abstract's claim that both paths are algebraically
+                     equivalent: equal to the absorbed form with per-head weights
+                     repeated over each group (1e-12); pure-Python brute force of the
+                     non-absorbed form with those weights; n_g = n_h reduces to the
+                     non-absorbed form (tests/test_oracle_gqla.py; mutants caught).
   mla_nonabsorbed    absorbed == non-absorbed identity; pure-Python brute force.
   mla_absorbed       torch SDPA in float64; brute force; closed forms.
   split_partial,
@@ -177,6 +183,53 @@ def fold_output_weights(w_o, w_uv):
     w_uv = np.asarray(w_uv, np.float64)
     n_h, d_v, _ = w_uv.shape
     return np.concatenate([w_o[:, i * d_v:(i + 1) * d_v] @ w_uv[i] for i in range(n_h)], axis=1)
+
+
+def gqla_expand(c, w_uk_g, w_uv_g):
+    """GQLA's per-group expanded cache.
+
+    [GQ] abstract: the same weights expose an MQA-absorb path identical to MLA's and a GQA
+    path with a per-group expanded cache.  Reading: heads are split into n_g equal groups
+    and the heads of group g share the up-projections W^UK_g, W^UV_g; the expanded cache of
+    token j holds k_{j,g} = W^UK_g c_j and v_{j,g} = W^UV_g c_j for every group (the
+    position key k^R_j stays shared).  c [L, d_c]; w_uk_g [n_g, d_h, d_c];
+    w_uv_g [n_g, d_v, d_c].  Returns k [L, n_g, d_h], v [L, n_g, d_v].
+    """
+    c = np.asarray(c, np.float64)
+    k = np.einsum("gkc,jc->jgk", np.asarray(w_uk_g, np.float64), c)
+    v = np.einsum("gvc,jc->jgv", np.asarray(w_uv_g, np.float64), c)
+    return k, v
+
+
+def gqla_decode(q_c, q_r, k_exp, v_exp, k_r, scale, n_vis):
+    """GQA decode of one query position over the per-group expanded cache.
+
+    Head i belongs to group g = i // (n_h / n_g); its key for token j is [k_{j,g} ; k^R_j]
+    and its value v_{j,g}; s_ij = scale (q^C_i . k_{j,g} + q^R_i . k^R_j) and
+    o_i = sum_j softmax_j(s_i)_j v_{j,g} ([AA] section 3: plain attention per head).
+    q_c [n_h, d_h], q_r [n_h, d_r], k_exp [L, n_g, d_h], v_exp [L, n_g, d_v], k_r [L, d_r].
+    Returns o [n_h, d_v] and lse [n_h].
+    """
+    q_c = np.asarray(q_c, np.float64)
+    q_r = np.asarray(q_r, np.float64)
+    k_exp = np.asarray(k_exp, np.float64)[:n_vis]
+    v_exp = np.asarray(v_exp, np.float64)[:n_vis]
+    k_r = np.asarray(k_r, np.float64)[:n_vis]
+    n_h = q_c.shape[0]
+    n_g = k_exp.shape[1]
+    per = n_h // n_g
+    o = np.zeros((n_h, v_exp.shape[2]))
+    lse = np.full(n_h, -np.inf)
+    if n_vis == 0:
+        return o, lse
+    for i in range(n_h):
+        g = i // per
+        s = scale * (k_exp[:, g, :] @ q_c[i] + k_r @ q_r[i])
+        m = s.max()
+        e = np.exp(s - m)
+        o[i] = (e / e.sum()) @ v_exp[:, g, :]
+        lse[i] = m + math.log(e.sum())
+    return o, lse
 
 
 # ----------------------------------------------------------------------------
