@@ -77,6 +77,12 @@ def parse():
                          "--copy-calibration-mb, print the attention kernel's HBM traffic per launch and record "
                          "it in profiles/attn_partial_traffic.json")
     ap.add_argument("--pmc-command", default="", help="command line recorded with --pmc-summary")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the attainable-peak probes (HBM streaming read, bf16 MFMA chains)")
+    ap.add_argument("--adjacent", action="store_true",
+                    help="instead of the decode step, time the adjacent rows at the V3 shape (cache write, query "
+                         "prologue, output projection unfolded and folded, GQLA per-group decode) and print one "
+                         "JSON line per row")
     return ap.parse_args()
 
 
@@ -337,10 +343,154 @@ def pmc_summary(args):
           f"{rec['attn_dispatches']} attention dispatches")
 
 
+def measured_peaks(dev):
+    """Attainable HBM read bandwidth (the attention kernel's buffer->LDS copy form over 4 GiB, cold)
+    and bf16 MFMA throughput (32x32x16 chains on every SIMD), with HIP events; best of 3."""
+    import ctypes
+    import torch
+    from mla_latent_kv_03_amd import build as _b
+    lib = ctypes.CDLL(_b.PEAKS_LIB)
+    lib.mla_peaks_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    lib.mla_peaks_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    wgs = 2048
+    nbytes = 4 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        best = None
+        for _ in range(4):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            if fn() != 0:
+                raise RuntimeError("peak probe launch failed")
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    ms_r = timed(lambda: lib.mla_peaks_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, wgs,
+                                                   ctypes.c_void_p(sink.data_ptr()), stream))
+    iters = 4096
+    ms_m = timed(lambda: lib.mla_peaks_mfma_bf16(ctypes.c_void_p(sink.data_ptr()), 1024, iters, stream))
+    del src
+    flops = 1024 * 4 * iters * 16 * 32768.0
+    return {"hbm_read_gbs": round(nbytes / (ms_r * 1e-3) / 1e9, 1), "bf16_mfma_tflops": round(flops / (ms_m * 1e-3) / 1e12, 1),
+            "method": "best of 4: 4 GiB streamed by 2048 workgroups of 16-byte buffer->LDS copies (streaming policy); "
+                      "1024 workgroups x 4 waves x 4 chains of 32x32x16 bf16 MFMAs"}
+
+
+def adjacent(args, dev):
+    """Time the rows adjacent to the decode step at the V3 shape (d_model 7168, 128 heads, d_c 512,
+    d_r 64, d_h = d_v = 128) on one batch of 64 new tokens, and GQLA's per-group decode; one JSON
+    line each with the algorithmic bytes (weights + activations read and written once) over the
+    event-timed duration against the 8 TB/s HBM peak.  Weight-streaming products are HBM-bound."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_03_amd import binding, workloads
+    B, D = 64, 7168
+    g = torch.Generator(device="cpu").manual_seed(6)
+    rnd = lambda *shape, std=1.0: (torch.randn(*shape, generator=g) * std).to(torch.bfloat16).to(dev)
+
+    def time_us(fn, reps=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    def line(row, what, us, nbytes):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        print(json.dumps({"row": row, "workload": what, "us": round(us, 2), "algorithmic_bytes": int(nbytes),
+                          "achieved_gbs": round(gbs, 1), "peak_gbs": HBM_PEAK_GBS,
+                          "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm", "dtype": "bf16"}), flush=True)
+
+    h = rnd(B, 1, D)
+    # cache write: [W^DKV; W^KR] h, RoPE, bf16 rows into a paged pool
+    x = workloads.make_decode([4096] * B, page_size=64, seed=7, **workloads.V3)
+    pool = x.pool.to(dev)
+    table = x.block_table.to(dev)
+    params = binding.params_for(x.q_nope, x.q_pe, pool[:, :512], pool[:, 512:], table, x.w_uv,
+                                softmax_scale=x.softmax_scale, page_size=64)
+    w_dkv, w_kr = rnd(512, D, std=D ** -0.5), rnd(64, D, std=D ** -0.5)
+    pos = torch.full((B, 1), 4095, dtype=torch.int32, device=dev)
+    ws = binding.alloc_workspace(params, dev)
+    cws = torch.empty(binding.LIB.mla_cache_write_workspace_size(ctypes_ref(params), D, 1), dtype=torch.uint8, device=dev)
+    us = time_us(lambda: binding.mla_cache_write(params, h, w_dkv, w_kr, pos, table, pool[:, :512], pool[:, 512:],
+                                                 workspace=cws))
+    line("f1 cache write", "V3: 64 tokens, d_model 7168 -> [c | RoPE k^R] bf16 rows", us,
+         (576 * D + B * D) * 2 + B * 576 * 2)
+    # query prologue: W^Q (16384 x 7168), W^QR (8192 x 7168), (W^UK)^T (128 x 512 x 128)
+    w_q, w_qr = rnd(128 * 128, D, std=D ** -0.5), rnd(128 * 64, D, std=D ** -0.5)
+    w_ukt = rnd(128, 512, 128, std=512 ** -0.5)
+    qws = torch.empty(binding.LIB.mla_query_prologue_workspace_size(ctypes_ref(params), D, 128), dtype=torch.uint8,
+                      device=dev)
+    qn = torch.empty(B, 1, 128, 512, dtype=torch.bfloat16, device=dev)
+    qp = torch.empty(B, 1, 128, 64, dtype=torch.bfloat16, device=dev)
+    us = time_us(lambda: binding.mla_query_prologue(params, h, w_q, w_ukt, w_qr, pos, qn, qp, d_h=128, workspace=qws),
+                 reps=10)
+    line("f2 query prologue", "V3: 64 tokens, W^Q 16384x7168, W^QR 8192x7168, W^UK 128x128x512", us,
+         (128 * 192 * D + 128 * 512 * 128 + B * D) * 2 + B * 128 * 576 * 2)
+    del w_q, w_qr
+    # output projection, unfolded (W^O 7168 x 16384 on o) and folded (W^OV 7168 x 65536 on u)
+    w_o = rnd(D, 128 * 128, std=(128 * 128) ** -0.5)
+    o = rnd(B, 1, 128, 128)
+    y = torch.empty(B, 1, D, dtype=torch.bfloat16, device=dev)
+    ows = torch.empty(binding.LIB.mla_output_projection_workspace_size(ctypes_ref(params), D, 128 * 128, binding.BF16),
+                      dtype=torch.uint8, device=dev)
+    us = time_us(lambda: binding.mla_output_projection(params, o, w_o, y, workspace=ows), reps=10)
+    line("f3 output projection (unfolded)", "V3: 64 rows, W^O 7168x16384 on the decode output", us,
+         (D * 128 * 128 + B * 128 * 128 + B * D) * 2)
+    w_ov = binding.mla_fold_output_weights(params, w_o, x.w_uv.to(dev))
+    u = torch.randn(B, 1, 128, 512, generator=g).to(dev)
+    fws = torch.empty(binding.LIB.mla_output_projection_workspace_size(ctypes_ref(params), D, 128 * 512, binding.F32),
+                      dtype=torch.uint8, device=dev)
+    us = time_us(lambda: binding.mla_output_projection(params, u, w_ov, y, workspace=fws), reps=5)
+    line("f3 output projection (folded)", "V3: 64 rows, W^OV 7168x65536 on float32 latents", us,
+         D * 128 * 512 * 2 + B * 128 * 512 * 4 + B * D * 2)
+    del w_ov, w_o
+    # GQLA per-group decode: 8 groups of 16 heads, s_q = 2, 32 sequences of 4096 tokens
+    xg = workloads.make_decode([4096] * 32, s_q=2, page_size=64, seed=8, **workloads.V3)
+    poolg = xg.pool.to(dev)
+    pg = binding.params_for(xg.q_nope, xg.q_pe, poolg[:, :512], poolg[:, 512:], xg.block_table, xg.w_uv,
+                            softmax_scale=xg.softmax_scale, page_size=64)
+    k_exp, v_exp = binding.mla_gqla_expand_cache(pg, rnd(8, 128, 512, std=512 ** -0.5), rnd(8, 128, 512, std=512 ** -0.5),
+                                                 poolg[:, :512])
+    q_c, q_pe = rnd(32, 2, 128, 128), xg.q_pe.to(dev)
+    bt, sl = xg.block_table.to(dev), xg.seq_lens.to(dev)
+    gws = torch.empty(binding.LIB.mla_gqla_decode_workspace_size(ctypes_ref(pg), 8, 128), dtype=torch.uint8, device=dev)
+    out = torch.empty(32, 2, 128, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(32, 2, 128, dtype=torch.float32, device=dev)
+    us = time_us(lambda: binding.mla_gqla_decode(pg, q_c, q_pe, k_exp, v_exp, poolg[:, 512:], bt, sl, out, lse,
+                                                 workspace=gws), reps=10)
+    tokens = 32 * 4096
+    line("f4 GQLA per-group decode", "32 sequences x 4096 tokens, s_q 2, 8 groups of 16 heads, d_h 128 + d_r 64, d_v 128",
+         us, tokens * 8 * (128 + 128 + 64) * 2 + 32 * 2 * 128 * (128 + 64) * 2)
+
+
+def ctypes_ref(params):
+    import ctypes
+    return ctypes.byref(params)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args)
+        return
+    if args.adjacent:
+        import torch
+        torch.cuda.set_device(0)
+        adjacent(args, "cuda:0")
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -436,6 +586,13 @@ def main():
             counted["traffic_gbs"] = round(traffic / (attn_ms * 1e-3) / 1e9, 1)
             if "mfma_busy_frac" in rec:
                 counted["mfma_busy_frac_counter"] = rec["mfma_busy_frac"]
+    peaks = None if args.no_peaks else measured_peaks(dev)
+    if peaks:
+        print(f"[bench] measured peaks: HBM read {peaks['hbm_read_gbs']:.0f} GB/s, bf16 MFMA "
+              f"{peaks['bf16_mfma_tflops']:.0f} TFLOP/s", file=sys.stderr, flush=True)
+        counted["measured_peaks"] = peaks
+        counted["frac_of_measured_hbm"] = round(attn_gbs / peaks["hbm_read_gbs"], 4)
+        counted["mfma_frac_of_measured"] = round(attn_tflops / peaks["bf16_mfma_tflops"], 4)
     roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": kname, "kernel_us": round(attn_ms * 1e3, 2),

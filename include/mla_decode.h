@@ -314,6 +314,37 @@ mla_status_t mla_fold_output_weights(const mla_decode_params_t* params, int32_t 
                                      void* stream);
 
 /*
+ * GQLA's per-group path (GQLA abstract, chatpaper.ai: the same weights expose an
+ * MQA-absorb path identical to MLA's and a GQA path with a per-group expanded cache).
+ * The n_h heads form n_g equal groups (heads g*n_h/n_g ..) that share W^UK_g and W^UV_g,
+ * so the absorbed path is mla_decode_fwd with q_nope_i = (W^UK_g)^T q^C_i and
+ * W^UV_i = W^UV_g, and the GQA path below reads instead a cache expanded per group.
+ *
+ * mla_gqla_expand_cache: for every pool slot s and group g,
+ *     k_exp[s][g][:] = W^UK_g c_s  (d_h values),  v_exp[s][g][:] = W^UV_g c_s  (d_v values),
+ * bf16 with float32 accumulation; w_uk_g [n_g, d_h, d_c], w_uv_g [n_g, d_v, d_c], c_kv the
+ * latent pool (slot s at c_kv + s * c_kv_stride), k_exp [num_pages * P, n_g, d_h],
+ * v_exp [num_pages * P, n_g, d_v].  The RoPE keys stay in the latent pool.
+ *
+ * mla_gqla_decode: per head i of group g and query position q (visibility as in
+ * mla_decode_fwd),
+ *     s_ij = softmax_scale (q_c_i . k_exp[j][g] + q_pe_i . k^R_j),
+ *     out_i = sum_j softmax_j(s_i) v_exp[j][g],   lse_i = ln sum_j exp(s_ij),
+ * with q_c [B, s_q, n_h, d_h], q_pe [B, s_q, n_h, d_r], k_pe the pool's RoPE keys, the
+ * block table and seq_lens of mla_decode_fwd, out [B, s_q, n_h, d_v] bf16 and lse
+ * [B, s_q, n_h] float (or NULL).  All dtypes bf16; n_h a multiple of n_g with
+ * (n_h / n_g) * s_q <= 32; (d_h + d_r, d_v) one of (192, 128), (64, 64), (32, 32).
+ * The workspace (mla_gqla_decode_workspace_size bytes) holds the split partials.
+ */
+mla_status_t mla_gqla_expand_cache(const mla_decode_params_t* params, int32_t n_g, int32_t d_h, const void* w_uk_g,
+                                   const void* w_uv_g, const void* c_kv, void* k_exp, void* v_exp, void* stream);
+size_t mla_gqla_decode_workspace_size(const mla_decode_params_t* params, int32_t n_g, int32_t d_h);
+mla_status_t mla_gqla_decode(const mla_decode_params_t* params, int32_t n_g, int32_t d_h, const void* q_c,
+                             const void* q_pe, const void* k_exp, const void* v_exp, const void* k_pe,
+                             const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mla_decode_fwd without a workspace argument, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Same arguments, results and validation as mla_decode_fwd, except:

@@ -23,7 +23,8 @@ EXPORTS = ("mla_decode_num_splits", "mla_decode_workspace_size", "mla_decode_fwd
            "mla_abi_version", "mla_decode_fwd_noalloc", "mla_decode_noalloc_capacity", "mla_cache_write",
            "mla_cache_write_workspace_size", "mla_query_prologue", "mla_query_prologue_workspace_size",
            "mla_output_projection", "mla_output_projection_workspace_size", "mla_fold_output_weights",
-           "mla_fold_output_weights_workspace_size")
+           "mla_fold_output_weights_workspace_size", "mla_gqla_expand_cache", "mla_gqla_decode",
+           "mla_gqla_decode_workspace_size")
 
 
 class DecodeParams(ctypes.Structure):
@@ -87,6 +88,12 @@ def _load():
     lib.mla_fold_output_weights_workspace_size.restype = sz
     lib.mla_fold_output_weights.argtypes = [P, i32, vp, vp, vp, vp, sz, vp]
     lib.mla_fold_output_weights.restype = ctypes.c_int
+    lib.mla_gqla_expand_cache.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.mla_gqla_expand_cache.restype = ctypes.c_int
+    lib.mla_gqla_decode_workspace_size.argtypes = [P, i32, i32]
+    lib.mla_gqla_decode_workspace_size.restype = sz
+    lib.mla_gqla_decode.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, i32p, i32p, vp, f32p, vp, sz, vp]
+    lib.mla_gqla_decode.restype = ctypes.c_int
     lib.mla_set_attention_events.argtypes = [vp, vp]
     lib.mla_set_attention_events.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -316,6 +323,39 @@ def mla_fold_output_weights(params, w_o, w_uv, w_ov=None):
                                        _ptr(workspace), workspace.numel(), _stream())
     _check(code, "mla_fold_output_weights")
     return w_ov
+
+
+def mla_gqla_expand_cache(params, w_uk_g, w_uv_g, c_kv, k_exp=None, v_exp=None):
+    """Per-group expanded cache of GQLA's GQA path: k_exp [slots, n_g, d_h], v_exp [slots, n_g, d_v]."""
+    n_g, d_h = w_uk_g.shape[0], w_uk_g.shape[1]
+    slots = params.num_pages * params.page_size
+    if k_exp is None:
+        k_exp = torch.empty(slots, n_g, d_h, dtype=torch.bfloat16, device=c_kv.device)
+    if v_exp is None:
+        v_exp = torch.empty(slots, n_g, params.d_v, dtype=torch.bfloat16, device=c_kv.device)
+    code = LIB.mla_gqla_expand_cache(ctypes.byref(params), int(n_g), int(d_h), _ptr(w_uk_g), _ptr(w_uv_g), _ptr(c_kv),
+                                     _ptr(k_exp), _ptr(v_exp), _stream())
+    _check(code, "mla_gqla_expand_cache")
+    return k_exp, v_exp
+
+
+def mla_gqla_decode(params, q_c, q_pe, k_exp, v_exp, k_pe, block_table, seq_lens, out=None, lse=None,
+                    workspace=None):
+    """GQA decode over the per-group expanded cache; returns (out [B, s_q, n_h, d_v], lse [B, s_q, n_h])."""
+    B, s_q, n_h, d_h = q_c.shape
+    n_g = k_exp.shape[1]
+    if out is None:
+        out = torch.empty(B, s_q, n_h, params.d_v, dtype=torch.bfloat16, device=q_c.device)
+    if lse is None:
+        lse = torch.empty(B, s_q, n_h, dtype=torch.float32, device=q_c.device)
+    if workspace is None:
+        workspace = _workspace(LIB.mla_gqla_decode_workspace_size(ctypes.byref(params), int(n_g), int(d_h)),
+                               "mla_gqla_decode_workspace_size", q_c.device)
+    code = LIB.mla_gqla_decode(ctypes.byref(params), int(n_g), int(d_h), _ptr(q_c), _ptr(q_pe), _ptr(k_exp),
+                               _ptr(v_exp), _ptr(k_pe), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
+                               _ptr(workspace), workspace.numel(), _stream())
+    _check(code, "mla_gqla_decode")
+    return out, lse
 
 
 def mla_set_attention_events(start=None, stop=None):

@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["mla_api.cpp", "mla_proj_api.cpp", "mla_attn_mfma.hip", "mla_attn_h128.hip", "mla_attn_fp8_v0.hip",
-           "mla_attn_f32.hip", "mla_combine.hip", "mla_append.hip", "mla_proj.hip"]
+           "mla_attn_f32.hip", "mla_combine.hip", "mla_append.hip", "mla_proj.hip", "mla_gqla.hip"]
 ARCH = "gfx950"
 
 
@@ -50,8 +50,26 @@ def _compile(src, verbose):
     return obj
 
 
+PEAKS_SRC = os.path.join(PKG, "peaks", "mla_peaks.hip")
+PEAKS_LIB = os.path.join(PKG, "peaks", "libmla_peaks.so")
+
+
+def build_peaks(verbose=False):
+    """The attainable-peak probes (bench.py --peaks), a library of their own."""
+    tmp = PEAKS_LIB + ".tmp"
+    cmd = [hipcc(), *compile_flags(), "-shared", "-x", "hip", PEAKS_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on mla_peaks.hip:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PEAKS_LIB)
+    return PEAKS_LIB
+
+
 def build(verbose=False):
-    """Compile every HIP source for gfx950 and link libmla_decode.so (always rebuilds)."""
+    """Compile every HIP source for gfx950 and link libmla_decode.so (always rebuilds), and the
+    peak probes."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
@@ -63,6 +81,7 @@ def build(verbose=False):
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
+    build_peaks(verbose)
     return LIB_PATH
 
 

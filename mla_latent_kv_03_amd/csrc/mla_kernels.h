@@ -108,6 +108,27 @@ struct QueryArgs {
   float rope_base;
 };
 
+// GQLA per-group decode (mla_gqla.hip): split partials [B][n_g][splits][32 rows][d_v] and
+// lse, merged into out [B, s_q, n_h, d_v] (bf16) and lse [B, s_q, n_h].
+struct GqaParams {
+  const void* q_c;           // [B, s_q, n_h, d_h] bf16
+  const void* q_pe;          // [B, s_q, n_h, d_r] bf16
+  const void* k_exp;         // [slots, n_g, d_h] bf16
+  const void* v_exp;         // [slots, n_g, d_v] bf16
+  const void* k_pe;          // pool of RoPE keys, slot s at k_pe + s * k_pe_stride
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* part_o;
+  float* part_lse;
+  void* out;
+  float* lse;
+  int64_t k_pe_stride;
+  int32_t batch, s_q, n_h, n_g, d_h, d_r, d_v;
+  int32_t page_size, num_pages, max_pages, max_tokens, chunk, splits;
+  float scale_log2;
+};
+hipError_t launch_gqa_decode(const GqaParams& p, hipStream_t s);
+
 hipError_t launch_gemm_nt(const GemmArgs& g, bool bf16_operands, int ksplit, hipStream_t s);
 hipError_t launch_cache_write_finish(const CacheWriteArgs& a, int tokens, hipStream_t s);
 hipError_t launch_query_finish(const QueryArgs& a, int tokens, hipStream_t s);

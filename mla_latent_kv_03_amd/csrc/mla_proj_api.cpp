@@ -325,3 +325,118 @@ mla_status_t mla_fold_output_weights(const mla_decode_params_t* params, int32_t 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- GQLA per-group path
+
+namespace {
+
+mla_status_t check_gqla(const mla_decode_params_t* p, int32_t n_g, int32_t d_h) {
+  if (!p) return MLA_ERR_NULL;
+  if (p->batch < 1 || p->s_q < 1 || p->n_h < 1 || n_g < 1 || d_h < 1 || p->d_r < 0 || p->d_c < 1 || p->d_v < 1)
+    return MLA_ERR_SHAPE;
+  if (p->n_h % n_g || (p->n_h / n_g) * p->s_q > 32) return MLA_ERR_SHAPE;
+  if (p->q_dtype != MLA_DTYPE_BF16 || p->kv_dtype != MLA_DTYPE_BF16 || p->w_dtype != MLA_DTYPE_BF16 ||
+      p->out_dtype != MLA_DTYPE_BF16)
+    return MLA_ERR_DTYPE;
+  const int kd = d_h + p->d_r;
+  if (!((kd == 192 && p->d_v == 128) || (kd == 32 && p->d_v == 32) || (kd == 64 && p->d_v == 64)))
+    return MLA_ERR_SHAPE;
+  if (d_h % 8 || p->d_r % 8 || p->d_c % 32) return MLA_ERR_SHAPE;
+  if (p->page_size < 64 || p->page_size % 64 || p->num_pages < 1 || p->max_pages_per_seq < 1) return MLA_ERR_SHAPE;
+  if ((long long)p->max_pages_per_seq * p->page_size > INT_MAX) return MLA_ERR_SHAPE;
+  if (p->c_kv_stride < p->d_c || p->k_pe_stride < p->d_r || p->c_kv_stride % 8 || p->k_pe_stride % 8)
+    return MLA_ERR_SHAPE;
+  if (!(p->softmax_scale > 0.f) || p->softmax_scale == INFINITY) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+// Token splits per sequence: enough (sequence, group, split) waves to fill the device
+// (>= 1024), chunks of at least 256 tokens, a multiple of 32.
+void gqla_splits(const mla_decode_params_t& p, int32_t n_g, int& splits, int& chunk) {
+  const long long max_tokens = (long long)p.max_pages_per_seq * p.page_size;
+  long long want = (1024 + (long long)p.batch * n_g - 1) / ((long long)p.batch * n_g);
+  const long long most = (max_tokens + 255) / 256;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  chunk = (int)(((max_tokens + want - 1) / want + 31) / 32 * 32);
+  splits = (int)((max_tokens + chunk - 1) / chunk);
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_gqla_expand_cache(const mla_decode_params_t* params, int32_t n_g, int32_t d_h, const void* w_uk_g,
+                                   const void* w_uv_g, const void* c_kv, void* k_exp, void* v_exp, void* stream) {
+  mla_status_t st = check_gqla(params, n_g, d_h);
+  if (st != MLA_OK) return st;
+  const mla_decode_params_t& p = *params;
+  if (!w_uk_g || !w_uv_g || !c_kv || !k_exp || !v_exp) return MLA_ERR_NULL;
+  if (!aligned16(w_uk_g) || !aligned16(w_uv_g) || !aligned16(c_kv)) return MLA_ERR_SHAPE;
+  if ((long long)p.num_pages * p.page_size > INT_MAX) return MLA_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  const int slots = p.num_pages * p.page_size;
+  // k_exp[slot][g][:] = W^UK_g c_slot and v_exp[slot][g][:] = W^UV_g c_slot: C[slots, n_g * d] =
+  // c[slots, d_c] W^T with W = [n_g * d, d_c] (the stacked group matrices).
+  Split one{1, p.d_c};
+  mla::GemmArgs g = gemm(c_kv, p.c_kv_stride, w_uk_g, p.d_c, k_exp, (int64_t)n_g * d_h, slots, n_g * d_h, p.d_c, one, 0);
+  g.out_bf16 = 1;
+  st = status_of(mla::launch_gemm_nt(g, true, 1, s));
+  if (st != MLA_OK) return st;
+  g = gemm(c_kv, p.c_kv_stride, w_uv_g, p.d_c, v_exp, (int64_t)n_g * p.d_v, slots, n_g * p.d_v, p.d_c, one, 0);
+  g.out_bf16 = 1;
+  return status_of(mla::launch_gemm_nt(g, true, 1, s));
+}
+
+size_t mla_gqla_decode_workspace_size(const mla_decode_params_t* params, int32_t n_g, int32_t d_h) {
+  if (check_gqla(params, n_g, d_h) != MLA_OK) return 0;
+  int splits, chunk;
+  gqla_splits(*params, n_g, splits, chunk);
+  const size_t rows = (size_t)params->batch * n_g * splits * 32;
+  return a256(rows * params->d_v * sizeof(float)) + a256(rows * sizeof(float));
+}
+
+mla_status_t mla_gqla_decode(const mla_decode_params_t* params, int32_t n_g, int32_t d_h, const void* q_c,
+                             const void* q_pe, const void* k_exp, const void* v_exp, const void* k_pe,
+                             const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status_t st = check_gqla(params, n_g, d_h);
+  if (st != MLA_OK) return st;
+  const mla_decode_params_t& p = *params;
+  if (!q_c || !k_exp || !v_exp || !block_table || !seq_lens || !out) return MLA_ERR_NULL;
+  if (p.d_r > 0 && (!q_pe || !k_pe)) return MLA_ERR_NULL;
+  if (!aligned16(q_c) || !aligned16(k_exp) || !aligned16(v_exp) || (p.d_r > 0 && (!aligned16(q_pe) || !aligned16(k_pe))))
+    return MLA_ERR_SHAPE;
+  const size_t need = mla_gqla_decode_workspace_size(params, n_g, d_h);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
+  mla::GqaParams g;
+  gqla_splits(p, n_g, g.splits, g.chunk);
+  const size_t rows = (size_t)p.batch * n_g * g.splits * 32;
+  g.q_c = q_c;
+  g.q_pe = q_pe ? q_pe : q_c;
+  g.k_exp = k_exp;
+  g.v_exp = v_exp;
+  g.k_pe = k_pe ? k_pe : k_exp;
+  g.block_table = block_table;
+  g.seq_lens = seq_lens;
+  g.part_o = (float*)workspace;
+  g.part_lse = (float*)((char*)workspace + a256(rows * p.d_v * sizeof(float)));
+  g.out = out;
+  g.lse = lse;
+  g.k_pe_stride = p.k_pe_stride;
+  g.batch = p.batch;
+  g.s_q = p.s_q;
+  g.n_h = p.n_h;
+  g.n_g = n_g;
+  g.d_h = d_h;
+  g.d_r = p.d_r;
+  g.d_v = p.d_v;
+  g.page_size = p.page_size;
+  g.num_pages = p.num_pages;
+  g.max_pages = p.max_pages_per_seq;
+  g.max_tokens = p.max_pages_per_seq * p.page_size;
+  g.scale_log2 = p.softmax_scale * 1.4426950408889634f;
+  return status_of(mla::launch_gqa_decode(g, (hipStream_t)stream));
+}
+
+}  // extern "C"
