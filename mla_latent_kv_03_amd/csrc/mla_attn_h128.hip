@@ -325,12 +325,13 @@ void attn_partial_h128(const AttnParams p) {
       pw_b = pc.b;
     }
     // Fused append: the tile (npt) and tile row (nrow) of each new row of this sequence
-    // that lies in the piece's visible tokens, else -1.  Wave-uniform.
+    // that lies in the piece's visible tokens, else -1.  Wave-uniform; the positions come
+    // through the scalar cache, so this wait does not also wait for the copies in flight.
     const bool fused = p.new_c != nullptr;
     int npt[kMaxFusedNew], nrow[kMaxFusedNew];
 #pragma unroll
     for (int i = 0; i < kMaxFusedNew; ++i) {
-      const int pos = fused && i < p.s_new ? p.new_pos[(size_t)pc.b * p.s_new + i] : -1;
+      const int pos = fused && i < p.s_new ? load_scalar(p.new_pos + (size_t)pc.b * p.s_new + i) : -1;
       const bool in = pos >= t0 && pos < end;
       npt[i] = in ? (pos - t0) / kT : -1;
       nrow[i] = in ? (pos - t0) % kT : -1;
@@ -379,9 +380,13 @@ void attn_partial_h128(const AttnParams p) {
 
     // Copy cursor: the next tile to enqueue, its logical page, its tile index within
     // that page and its ring slots.
-    int i_tt, i_lp, i_tip, i_vs, i_ks;
+    // pg_lp / pg_id: the last logical page looked up and its id (a page holds several
+    // tiles, and a lookup is a register read plus scalar checks).
+    int i_tt, i_lp, i_tip, i_vs, i_ks, pg_lp, pg_id;
     auto reset_cursor = [&]() {
       pw.rewind(t0 / p.page_size);
+      pg_lp = -1;
+      pg_id = -1;
       i_tt = t0;
       i_lp = t0 / p.page_size;
       i_tip = (t0 - i_lp * p.page_size) / kT;
@@ -401,7 +406,11 @@ void attn_partial_h128(const AttnParams p) {
     // whether the tile has a valid page.
     auto prepare_next = [&](bool exists, bool& ok) {
       TileCopy tc;
-      const int page = exists ? pw.get(i_lp) : -1;
+      if (exists && i_lp != pg_lp) {
+        pg_id = pw.get(i_lp);
+        pg_lp = i_lp;
+      }
+      const int page = exists ? pg_id : -1;
       ok = page >= 0;
       const long long slot0 = ok ? (long long)page * p.page_size + i_tip * kT : 0;
       tc.vres = buffer_rsrc((const char*)p.c_kv + slot0 * c_row, ok ? 0x7fffffff : 0);
@@ -695,60 +704,86 @@ void attn_partial_h128(const AttnParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
         const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
-        float x[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) x[v] = __builtin_fmaf(s[v], p.scale_log2, nm);
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) x_max = fmaxf(x_max, fmaxf(x[v], x[v + 1]));
-        float psum = 0.f, esum = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          x[v] = exp2_fast(x[v]);
-          psum += x[v];
-        }
-        if constexpr (FP8) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) x[v] *= tsc[v >> 2][v & 3];
-        }
-        // Token half `half` of this lane's probabilities is the B operand (head block
-        // `wave`, token half `half`) of the accumulation: store it as is.
+        // Phase 2: the other 16 accumulation MFMAs of tile it-1, each followed by a fixed
+        // share of the softmax of tile `it` (scale and shift, exponentials, running maximum,
+        // bf16 packing and the exchange-buffer stores, the row-sum tree).  The groups keep
+        // this order (scheduling barriers), so no run of exponentials or of dependent adds
+        // holds up the next MFMA, and every operand was produced at least one group earlier.
+        //
+        // Token half h of this lane's probabilities is the B operand (head block `wave`,
+        // token half h) of the accumulation: it is stored as is.
+        // E4M3: the weight that reaches the accumulation is the bf16 rounding w~ of p * scale,
+        // so U is divided by the sum of w~ / scale over the same tokens.  Numerator and
+        // denominator then agree, and the rounding only perturbs each token's weight by its
+        // relative rounding error, as with a bf16 cache; dividing by the sum of the unrounded
+        // p instead would scale the whole row by the rounding error of one token's scale when
+        // that token dominates.  The lse keeps the unrounded sum (it weights this piece
+        // against the others).  A token whose scale is 0 (a tile with no valid page) has
+        // w~ = 0.
         unsigned char* pout = (unsigned char*)&sm + lo.pb + (it & 1) * kPBuf + wave * 2 * 1024;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8 pf;
+        float x[16], e[16], mx[8], ps[8], rs[FP8 ? 16 : 1];
+        bf16x8 pf[2];
+        float esum = 0.f;
+        auto pack_half = [&](int h) {
 #pragma unroll
           for (int j = 0; j < 8; j += 2) {
-            const bf16x2 t = pack_bf16(x[8 * half + j], x[8 * half + j + 1]);
-            pf[j] = t[0];
-            pf[j + 1] = t[1];
+            const float w0 = FP8 ? e[8 * h + j] * tsc[(8 * h + j) >> 2][j & 3] : e[8 * h + j];
+            const float w1 = FP8 ? e[8 * h + j + 1] * tsc[(8 * h + j + 1) >> 2][(j + 1) & 3] : e[8 * h + j + 1];
+            const bf16x2 t = pack_bf16(w0, w1);
+            pf[h][j] = t[0];
+            pf[h][j + 1] = t[1];
           }
-          *(bf16x8*)(pout + half * 1024) = pf;
-          if constexpr (FP8) {
-            // E4M3: the weight that reaches the accumulation is the bf16 rounding w~ of
-            // p * scale, so U is divided by the sum of w~ / scale over the same tokens.
-            // Numerator and denominator then agree, and the rounding only perturbs each
-            // token's weight by its relative rounding error, as with a bf16 cache; dividing
-            // by the sum of the unrounded p instead would scale the whole row by the
-            // rounding error of one token's scale when that token dominates.  The lse keeps
-            // the unrounded sum (it weights this piece against the others).  A token whose
-            // scale is 0 (a tile with no valid page) has w~ = 0.
+          *(bf16x8*)(pout + h * 1024) = pf[h];
+        };
+        auto eff_sum = [&](int h, int j0) {   // E4M3: w~ / scale of tokens 8h + j0 .. + 3
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float sc = tsc[(8 * half + j) >> 2][j & 3];
-              const float r = fminf(__builtin_amdgcn_rcpf(sc), 3.0e38f);
-              esum = __builtin_fmaf((float)pf[j], r, esum);
+          for (int j = j0; j < j0 + 4; ++j) esum = __builtin_fmaf((float)pf[h][j], rs[8 * h + j], esum);
+        };
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          __builtin_amdgcn_sched_barrier(0);
+          acc[g] = mfma32(va[g / 4], pb[1][g % 4], acc[g]);
+          if (g < 4) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              x[4 * g + j] = __builtin_fmaf(s[4 * g + j], p.scale_log2, nm);
+              if constexpr (FP8) rs[4 * g + j] = fminf(__builtin_amdgcn_rcpf(tsc[g][j]), 3.0e38f);
             }
+          } else if (g < 12) {
+            const int k = g - 4;
+            e[2 * k] = exp2_fast(x[2 * k]);
+            e[2 * k + 1] = exp2_fast(x[2 * k + 1]);
+            if (k < 4) {
+              mx[2 * k] = fmaxf(x[4 * k], x[4 * k + 1]);
+              mx[2 * k + 1] = fmaxf(x[4 * k + 2], x[4 * k + 3]);
+            } else if (k == 4) {
+              mx[0] = fmaxf(fmaxf(mx[0], mx[1]), mx[2]);
+              mx[3] = fmaxf(fmaxf(mx[3], mx[4]), mx[5]);
+            } else if (k == 5) {
+              x_max = fmaxf(fmaxf(x_max, mx[0]), fmaxf(mx[3], fmaxf(mx[6], mx[7])));
+            } else if (k == 6) {
+              pack_half(0);                  // e[0..7] exist since k = 3
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) ps[j] = e[2 * j] + e[2 * j + 1];
+            }
+          } else if (g == 12) {
+            pack_half(1);                    // e[14], e[15] exist since g = 11
+            if constexpr (FP8) eff_sum(0, 0);
+          } else if (g == 13) {
+#pragma unroll
+            for (int j = 4; j < 8; ++j) ps[j] = e[2 * j] + e[2 * j + 1];
+            if constexpr (FP8) eff_sum(0, 4);
+          } else if (g == 14) {
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) ps[j] += ps[j + 1];
+            if constexpr (FP8) eff_sum(1, 0);
+          } else {
+            const float psum = (ps[0] + ps[2]) + (ps[4] + ps[6]);
+            if constexpr (FP8) eff_sum(1, 4);
+            l_part += psum;
+            l_eff += FP8 ? esum : psum;
           }
-        }
-        l_part += psum;
-        l_eff += FP8 ? esum : psum;
-#pragma unroll
-        for (int a = 16; a < kPv; ++a) acc[a - 16] = mfma32(va[(a - 16) / 4], pb[1][a % 4], acc[a - 16]);
-        // Interleave: one accumulation MFMA, then a share of the softmax.
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
         }
         __builtin_amdgcn_sched_barrier(0);
 
