@@ -397,13 +397,25 @@ def adjacent(args, dev):
     rnd = lambda *shape, std=1.0: (torch.randn(*shape, generator=g) * std).to(torch.bfloat16).to(dev)
 
     def time_us(fn, reps=20):
+        """GPU time of one call: the call's launches are captured once in a HIP graph (on a
+        side stream) and the graph is replayed `reps` times between two events, so that the
+        host-side marshalling of each call is not counted."""
         for _ in range(3):
             fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        graph.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
-            fn()
+            graph.replay()
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / reps

@@ -8,7 +8,8 @@
 //
 // One wave per (sequence, group, token split): its rows are the group's heads at every query
 // position (row = q * heads_per_group + head, at most 32), 32-token tiles are staged in LDS
-// (keys [k_g | k^R] and values v_g, rows padded by 16 bytes against bank conflicts), the
+// through a register prefetch of the next tile (keys [k_g | k^R] and values v_g, rows
+// padded by 16 bytes against bank conflicts), the
 // scores S^T[token, row] run on 32x32x16 bf16 MFMAs, an online softmax (running maximum,
 // rescaled accumulators) feeds U^T[col, row] += V^T P^T, where each lane's probabilities are
 // already its B operand and transposed LDS reads give the V^T operand in the same token order.
@@ -25,6 +26,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kGT = 32;            // tokens per tile
 constexpr int kGMaxKD = 256;       // d_h + d_r
 constexpr int kGMaxVD = 256;       // d_v
+
+// Orders this workgroup's LDS writes before its LDS reads without waiting for the global
+// loads in flight (a full __syncthreads would also wait for the prefetch of the next tile).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
 
 __device__ __forceinline__ f32x16 mfma32x32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -70,32 +78,55 @@ __global__ __launch_bounds__(64) void gqa_decode_partial(const GqaParams p) {
     for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int tt = t0; tt < t1; tt += kGT) {
-    // Stage the tile: 16-byte chunks of [k_g | k^R] and v_g rows; tokens past t1 or on an
-    // invalid page are zero-filled (and masked below).
-    constexpr int KC = KD / 8, VC = VD / 8;
-    for (int e = lane; e < kGT * (KC + VC); e += 64) {
-      const int tok = e < kGT * KC ? e / KC : (e - kGT * KC) / VC;
-      const int c = e < kGT * KC ? e % KC : (e - kGT * KC) % VC;
-      const int t = tt + tok;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (t < t1) {
-        const int pidx = t / p.page_size;
-        const int page = p.block_table[(size_t)b * p.max_pages + pidx];
-        if (page >= 0 && page < p.num_pages) {
-          const size_t slot = (size_t)page * p.page_size + t % p.page_size;
-          if (e < kGT * KC) {
-            v = 8 * c < p.d_h ? *(const u32x4*)((const bf16*)p.k_exp + (slot * p.n_g + g) * p.d_h + 8 * c)
-                              : *(const u32x4*)((const bf16*)p.k_pe + slot * p.k_pe_stride + (8 * c - p.d_h));
-          } else {
-            v = *(const u32x4*)((const bf16*)p.v_exp + (slot * p.n_g + g) * VD + 8 * c);
-          }
-        }
-      }
-      if (e < kGT * KC) *(u32x4*)(ks_lds + tok * KROW + 16 * c) = v;
-      else *(u32x4*)(vs_lds + tok * VROW + 16 * c) = v;
+  // Tile staging: a 32-token tile lies in one page (tiles start at multiples of 32 and
+  // pages hold a multiple of 64 tokens), so one scalar page lookup gives the base slot.
+  // Lane l holds 16-byte chunks e = l + 64 i of the tile ([k_g | k^R] rows, then v_g
+  // rows); the next tile's chunks are loaded into registers while this one is computed.
+  // Tokens past t1 or on an invalid page are zero-filled (and masked below).
+  constexpr int KC = KD / 8, VC = VD / 8;
+  constexpr int kChunks = kGT * (KC + VC);
+  constexpr int kPer = (kChunks + 63) / 64;
+  u32x4 pre[kPer];
+  auto fetch = [&](int tt) {
+    int page = -1;
+    if (tt < t1) {
+      page = load_scalar(p.block_table + (size_t)b * p.max_pages + tt / p.page_size);
+      if (page < 0 || page >= p.num_pages) page = -1;
     }
-    __syncthreads();
+    const size_t slot0 = page >= 0 ? (size_t)page * p.page_size + tt % p.page_size : 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = lane + 64 * i;
+      const bool kpart = e < kGT * KC;
+      const int tok = kpart ? e / KC : (e - kGT * KC) / VC;
+      const int c = kpart ? e % KC : (e - kGT * KC) % VC;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (e < kChunks && page >= 0 && tt + tok < t1) {
+        const size_t slot = slot0 + tok;
+        if (kpart)
+          v = 8 * c < p.d_h ? *(const u32x4*)((const bf16*)p.k_exp + (slot * p.n_g + g) * p.d_h + 8 * c)
+                            : *(const u32x4*)((const bf16*)p.k_pe + slot * p.k_pe_stride + (8 * c - p.d_h));
+        else
+          v = *(const u32x4*)((const bf16*)p.v_exp + (slot * p.n_g + g) * VD + 8 * c);
+      }
+      pre[i] = v;
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = lane + 64 * i;
+      if (e >= kChunks) continue;
+      if (e < kGT * KC) *(u32x4*)(ks_lds + (e / KC) * KROW + 16 * (e % KC)) = pre[i];
+      else *(u32x4*)(vs_lds + ((e - kGT * KC) / VC) * VROW + 16 * ((e - kGT * KC) % VC)) = pre[i];
+    }
+  };
+
+  if (t0 < t1) fetch(t0);
+  for (int tt = t0; tt < t1; tt += kGT) {
+    stage();
+    fetch(tt + kGT);   // the next tile's loads fly while this one is computed (none past t1)
+    lds_sync();
     // S^T[token, row]: lane holds token 8(v/4) + 4h + v%4 of row l32.
     f32x16 s;
 #pragma unroll
@@ -152,7 +183,7 @@ __global__ __launch_bounds__(64) void gqa_decode_partial(const GqaParams p) {
         acc[c] = mfma32x32(concat4(lo, hi), pf, acc[c]);
       }
     }
-    __syncthreads();
+    lds_sync();
   }
   // Partial of this split: u = U / l per row and its lse (natural log); an empty split gives
   // lse = -inf, o = 0.  Lane holds U^T[32c + 8(v/4) + 4h + v%4][l32].

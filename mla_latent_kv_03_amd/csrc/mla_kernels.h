@@ -81,9 +81,8 @@ struct GemmArgs {
 // Cache write finish: sums the partials [ksplit][T][d_c + d_r] of each new token's row,
 // rotates its RoPE part and writes the pool slot.
 struct CacheWriteArgs {
-  const float* part;
-  int64_t part_ks;
-  int32_t ksplit, d_c, d_r, s_new;
+  const float* part;         // summed rows [T][d_c + d_r]
+  int32_t d_c, d_r, s_new;
   const int32_t* positions;
   const int32_t* block_table;
   void* c_kv;
@@ -130,6 +129,10 @@ struct GqaParams {
 hipError_t launch_gqa_decode(const GqaParams& p, hipStream_t s);
 
 hipError_t launch_gemm_nt(const GemmArgs& g, bool bf16_operands, int ksplit, hipStream_t s);
+// Geometry of the bf16 product kernel, shared with the host-side K-split choice: blocks of
+// 32 rows of A per row tile (1 or 2), and of 32 rows of B per wave (float32 A: 2).
+inline int gemm_row_blocks(int M) { return M > 32 ? 2 : 1; }
+inline int gemm_col_blocks(bool a_f32) { return a_f32 ? 2 : 1; }
 hipError_t launch_cache_write_finish(const CacheWriteArgs& a, int tokens, hipStream_t s);
 hipError_t launch_query_finish(const QueryArgs& a, int tokens, hipStream_t s);
 hipError_t launch_sum_partials(const float* part, int64_t part_ks, int ksplit, int64_t n, void* out, bool out_bf16,

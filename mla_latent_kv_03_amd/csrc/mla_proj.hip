@@ -7,9 +7,9 @@
 //   output projection y = W x with x = o (W = W^O) or x = u (W = W^OV, the folded weights),
 //                     and the fold itself, W^OV_i = W^O_i W^UV_i.
 // Every product is C = A B^T with the contraction index contiguous in both operands.
-// bf16 operands run on 16x16x32 MFMAs, split over K into float32 partials that a finishing
-// kernel sums together with the row's own epilogue; float32 operands (small layers) use
-// plain FMA loops with the same partial layout.
+// bf16 weights run on 32x32x16 MFMAs in a weight-streaming kernel, split over K into
+// float32 partials that a finishing kernel sums together with the row's own epilogue;
+// float32 operands (small layers) use plain FMA loops with the same partial layout.
 
 #include "mla_device.h"
 #include "mla_kernels.h"
@@ -17,102 +17,174 @@
 namespace mla {
 namespace {
 
-constexpr int kGemmWaves = 4;
-constexpr int kTileN = 16 * kGemmWaves;   // columns per workgroup (16 per wave)
-constexpr int kTileM = 64;                // rows per workgroup (4 MFMA row blocks)
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// C[M, N] (+)= A[M, K] B[N, K]^T over K chunk blockIdx.y, for batch / row tile blockIdx.z.
-// Wave w owns columns n0 .. n0 + 15 of the workgroup's tile and all 64 rows: per 32-wide
-// k-step it loads one B fragment (16 rows of B, 8 consecutive k each: 16 bytes per lane)
-// and four A fragments (rows clamped to M - 1; such rows are never stored), and issues four
-// MFMAs.  B is read from memory exactly once per row tile; A comes from the caches.
-// A_F32: A is float32 and enters as a bf16 high part plus a bf16 remainder (two MFMAs).
-template <bool A_F32>
-__global__ __launch_bounds__(64 * kGemmWaves) void gemm_nt_bf16(const GemmArgs g) {
+constexpr int kGemmWaves = 4;
+
+// C[M, N] (+)= A[M, K] B[N, K]^T for bf16 B (the weights) and bf16 or float32 A (the few
+// activation rows of a decode step), built to stream B from HBM once at full rate.
+//
+// A workgroup of four waves covers 4 NB blocks of 32 rows of B, a K chunk (blockIdx.y)
+// and a row tile of A (blockIdx.z: MB blocks of 32 rows, rows past M clamped to M - 1 and
+// never stored).  Per 16-wide k-step each wave loads 16 bytes of each of its B rows into
+// a register ring of D steps (loads run D steps ahead of their MFMAs) and issues NB x MB
+// 32x32x16 MFMAs, with A rows as the first operand and B rows as the second, so that lane
+// l ends up holding C[8(v/4) + 4(l/32) + v%4][l%32] and each 32-lane half stores 128
+// contiguous bytes of a C row.
+// A is read from the caches once per workgroup, not once per wave (measured: every wave
+// re-reading its A fragments from the L2 held the B stream to about a third of the HBM
+// rate): blocks of 4 k-steps of A are staged in LDS in MFMA fragment order (fragment
+// (step, m-block) = 64 lanes x 16 bytes, float32 A: two such halves), three blocks deep;
+// each wave loads its share of block b + 2 into registers while block b is computed and
+// stores it after the next barrier, so one barrier per block orders everything.  Steps
+// past the chunk read the chunk's last B step and zero A, so whole rounds run unguarded.
+// AF32: A enters as a bf16 high part plus a bf16 remainder (two MFMAs per pair).
+template <int NB, int MB, bool AF32, int D>
+__global__ __launch_bounds__(64 * kGemmWaves) void gemm_stream(const GemmArgs g) {
+  static_assert(D == 8, "the round is two A blocks of four steps");
+  constexpr int kFrag = 1024 * (AF32 ? 2 : 1);   // bytes of one A fragment
+  constexpr int kSlot = 4 * MB * kFrag;          // one A block
+  __shared__ __attribute__((aligned(16))) unsigned char a_lds[3 * kSlot];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int l16 = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * kTileN + 16 * wave;
-  if (n0 >= g.N) return;                         // wave-uniform; the kernel has no barrier
-  const int mtiles = (g.M + kTileM - 1) / kTileM;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int n0 = (blockIdx.x * kGemmWaves + wave) * 32 * NB;   // waves past N still stage A
+  constexpr int kRows = 32 * MB;
+  const int mtiles = (g.M + kRows - 1) / kRows;
   const int bt = blockIdx.z / mtiles;
-  const int m0 = (blockIdx.z - bt * mtiles) * kTileM;
+  const int m0 = (blockIdx.z - bt * mtiles) * kRows;
   const int k0 = blockIdx.y * g.kchunk;
   const int k1 = min(g.K, k0 + g.kchunk);
-  const bf16* brow = (const bf16*)g.b + bt * g.b_bs + (int64_t)(n0 + l16) * g.ldb + 8 * grp;
-  int64_t arow[4];
+  const int nsteps = (k1 - k0) >> 4;
+  if (nsteps <= 0) return;                       // workgroup-uniform
+  const int nrounds = (nsteps + 7) >> 3;
+  const bf16* bp[NB];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) arow[mb] = bt * g.a_bs + (int64_t)min(m0 + 16 * mb + l16, g.M - 1) * g.lda + 8 * grp;
-  f32x4 acc[4];
+  for (int nb = 0; nb < NB; ++nb)
+    bp[nb] = (const bf16*)g.b + bt * g.b_bs + (int64_t)min(n0 + 32 * nb + l32, g.N - 1) * g.ldb + k0 + 8 * kh;
+  // This wave's A fragments of every block: f = wave + 4 j (j < MB), step f / MB, m-block
+  // f % MB; arow[j] is the start of the fragment's A row.
+  int64_t arow[MB];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Operands of one 32-wide k-step: the B fragment and the four A fragments (float32 A:
-  // two 16-byte halves per fragment, split into bf16 high and remainder parts at use).
-  struct Step {
-    bf16x8 b;
-    u32x4 a[4][A_F32 ? 2 : 1];
-  };
-  auto load = [&](int k, Step& st) {
-    st.b = *(const bf16x8*)(brow + k);
+  for (int j = 0; j < MB; ++j) {
+    const int mb = (wave + 4 * j) % MB;
+    arow[j] = bt * g.a_bs + (int64_t)min(m0 + 32 * mb + l32, g.M - 1) * g.lda;
+  }
+  u32x4 ar[MB][AF32 ? 2 : 1];
+  auto load_a = [&](int blk) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if constexpr (A_F32) {
-        const float* ap = (const float*)g.a + arow[mb] + k;
-        st.a[mb][0] = *(const u32x4*)ap;
-        st.a[mb][A_F32 ? 1 : 0] = *(const u32x4*)(ap + 4);
+    for (int j = 0; j < MB; ++j) {
+      const int f = wave + 4 * j;
+      const int k = k0 + 64 * blk + 16 * (f / MB) + 8 * kh;   // 8 values; the chunk ends on a multiple of 16
+      const bool in = k < k1;
+      const int64_t off = arow[j] + (in ? k : k0);            // past the chunk: an in-bounds read, zeroed
+      if constexpr (AF32) {
+        const float* x = (const float*)g.a + off;
+        ar[j][0] = *(const u32x4*)x;
+        ar[j][AF32 ? 1 : 0] = *(const u32x4*)(x + 4);
+        if (!in) ar[j][0] = ar[j][AF32 ? 1 : 0] = u32x4{0u, 0u, 0u, 0u};
       } else {
-        st.a[mb][0] = *(const u32x4*)((const bf16*)g.a + arow[mb] + k);
+        ar[j][0] = *(const u32x4*)((const bf16*)g.a + off);
+        if (!in) ar[j][0] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
-  auto compute = [&](const Step& st) {
+  auto store_a = [&](int slot) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if constexpr (A_F32) {
-        const f32x4 x0 = __builtin_bit_cast(f32x4, st.a[mb][0]), x1 = __builtin_bit_cast(f32x4, st.a[mb][A_F32 ? 1 : 0]);
+    for (int j = 0; j < MB; ++j) {
+      unsigned char* dst = a_lds + slot * kSlot + (wave + 4 * j) * kFrag + 16 * lane;
+      *(u32x4*)dst = ar[j][0];
+      if constexpr (AF32) *(u32x4*)(dst + 1024) = ar[j][AF32 ? 1 : 0];
+    }
+  };
+  f32x16 acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[nb][mb][v] = 0.f;
+  bf16x8 ring[D][NB];
+  auto load_w = [&](int step, bf16x8* w) {
+    const int k = 16 * min(step, nsteps - 1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) w[nb] = *(const bf16x8*)(bp[nb] + k);
+  };
+  // Step j (0..3) of the block in `slot`, with B fragments w.
+  auto compute = [&](int slot, int j, const bf16x8* w) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const unsigned char* src = a_lds + slot * kSlot + (j * MB + mb) * kFrag + 16 * lane;
+      if constexpr (AF32) {
+        const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 1024);
         bf16x8 hi, lo;
 #pragma unroll
-        for (int j = 0; j < 4; j += 2) {
-          const bf16x2 h0 = pack_bf16(x0[j], x0[j + 1]), h1 = pack_bf16(x1[j], x1[j + 1]);
-          const bf16x2 r0 = pack_bf16(x0[j] - (float)h0[0], x0[j + 1] - (float)h0[1]);
-          const bf16x2 r1 = pack_bf16(x1[j] - (float)h1[0], x1[j + 1] - (float)h1[1]);
-          hi[j] = h0[0]; hi[j + 1] = h0[1]; hi[4 + j] = h1[0]; hi[5 + j] = h1[1];
-          lo[j] = r0[0]; lo[j + 1] = r0[1]; lo[4 + j] = r1[0]; lo[5 + j] = r1[1];
+        for (int i = 0; i < 4; i += 2) {
+          const bf16x2 h0 = pack_bf16(x0[i], x0[i + 1]), h1 = pack_bf16(x1[i], x1[i + 1]);
+          const bf16x2 r0 = pack_bf16(x0[i] - (float)h0[0], x0[i + 1] - (float)h0[1]);
+          const bf16x2 r1 = pack_bf16(x1[i] - (float)h1[0], x1[i + 1] - (float)h1[1]);
+          hi[i] = h0[0]; hi[i + 1] = h0[1]; hi[4 + i] = h1[0]; hi[5 + i] = h1[1];
+          lo[i] = r0[0]; lo[i + 1] = r0[1]; lo[4 + i] = r1[0]; lo[5 + i] = r1[1];
         }
-        acc[mb] = mfma16x16x32(hi, st.b, acc[mb]);
-        acc[mb] = mfma16x16x32(lo, st.b, acc[mb]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, w[nb], acc[nb][mb], 0, 0, 0);
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, w[nb], acc[nb][mb], 0, 0, 0);
+        }
       } else {
-        acc[mb] = mfma16x16x32(__builtin_bit_cast(bf16x8, st.a[mb][0]), st.b, acc[mb]);
+        const bf16x8 a = *(const bf16x8*)src;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w[nb], acc[nb][mb], 0, 0, 0);
       }
     }
   };
-  // Four k-steps per round, all loads issued before the MFMAs that use them.
-  int k = k0;
-  for (; k + 128 <= k1; k += 128) {
-    Step st[4];
+
+  load_a(0);
+  store_a(0);
+  load_a(1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load(k + 32 * j, st[j]);
+  for (int j = 0; j < D; ++j) load_w(j, ring[j]);
+  for (int r = 0; r < nrounds; ++r) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) compute(st[j]);
-  }
-  for (; k < k1; k += 32) {
-    Step st;
-    load(k, st);
-    compute(st);
-  }
-  // Lane holds C[row 16 mb + 4 grp + i][column n0 + l16].
-  const int64_t cbase = (int64_t)blockIdx.y * g.c_ks + bt * g.c_bs + n0 + l16;
+    for (int h = 0; h < 2; ++h) {
+      const int blk = 2 * r + h;
+      __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): this wave's A stores are done
+      __builtin_amdgcn_s_barrier();                // A(blk) is in LDS; block blk - 1 is finished
+      __builtin_amdgcn_sched_barrier(0);
+      store_a((blk + 1) % 3);
+      load_a(blk + 2);
+      const int slot = blk % 3;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 16 * mb + 4 * grp + i;
-      if (m >= g.M) continue;
-      if (g.out_bf16)
-        ((bf16*)g.c)[cbase + (int64_t)m * g.ldc] = (bf16)acc[mb][i];
-      else
-        ((float*)g.c)[cbase + (int64_t)m * g.ldc] = acc[mb][i];
+      for (int j = 0; j < 4; ++j) {
+        // Keep the program order: the scheduler would otherwise sink the loads below the
+        // MFMAs and drain the ring once per round.
+        __builtin_amdgcn_sched_barrier(0);
+        compute(slot, j, ring[4 * h + j]);
+        load_w(8 * r + 4 * h + j + D, ring[4 * h + j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  if (n0 >= g.N) return;
+  // Lane holds C[m0 + 32 mb + 8 (v/4) + 4 kh + v%4][n0 + 32 nb + l32].
+  const int64_t cbase = (int64_t)blockIdx.y * g.c_ks + bt * g.c_bs;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = n0 + 32 * nb + l32;
+    if (n >= g.N) continue;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + 32 * mb + 8 * (v >> 2) + 4 * kh + (v & 3);
+        if (m >= g.M) continue;
+        if (g.out_bf16)
+          ((bf16*)g.c)[cbase + (int64_t)m * g.ldc + n] = (bf16)acc[nb][mb][v];
+        else
+          ((float*)g.c)[cbase + (int64_t)m * g.ldc + n] = acc[nb][mb][v];
+      }
+  }
 }
 
 // float32 operands: thread (m, n) of a 4 x 64 tile sums its K chunk with FMAs.
@@ -148,9 +220,10 @@ __device__ __forceinline__ float rope_lane(float v, int pair, int d_r, int pos, 
 
 constexpr int kMaxRowPerLane = 20;   // d_c + d_r <= 1280
 
-// One wave per new token: sums the K-split partials of its [c | k^R_raw] row, rotates the
-// RoPE part at the token's position and writes the pool slot (same slot rule and skips as
-// the append kernel; same E4M3 quantizer).
+// One wave per new token: reads its summed [c | k^R_raw] row (float32; the K-split
+// partials are added by sum_partials first), rotates the RoPE part at the token's position
+// and writes the pool slot (same slot rule and skips as the append kernel; same E4M3
+// quantizer).
 __global__ __launch_bounds__(64) void cache_write_finish(const CacheWriteArgs a) {
   const int tok = blockIdx.x;
   const int b = tok / a.s_new;
@@ -167,10 +240,7 @@ __global__ __launch_bounds__(64) void cache_write_finish(const CacheWriteArgs a)
 #pragma unroll
   for (int j = 0; j < kMaxRowPerLane; ++j) {
     const int e = lane + 64 * j;
-    float s = 0.f;
-    if (e < D)
-      for (int ks = 0; ks < a.ksplit; ++ks) s += a.part[(int64_t)ks * a.part_ks + (int64_t)tok * D + e];
-    v[j] = s;
+    v[j] = e < D ? a.part[(int64_t)tok * D + e] : 0.f;
   }
 #pragma unroll
   for (int j = 0; j < kMaxRowPerLane; ++j) {
@@ -217,30 +287,34 @@ __global__ __launch_bounds__(64) void cache_write_finish(const CacheWriteArgs a)
   if (lane == 0) a.kv_scale[slot] = scale;
 }
 
-// One wave per new query token: sums the K-split partials of q^C (to float32 scratch for the
-// absorption product) and of q^R_raw, and writes q^R = RoPE(q^R_raw) per head.
-__global__ __launch_bounds__(64) void query_finish(const QueryArgs a) {
-  const int tok = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int pos = a.positions[tok];
-  const int nc = a.n_h * a.d_h, nr = a.n_h * a.d_r;
-  for (int e = lane; e < nc; e += 64) {
-    float s = 0.f;
-    for (int ks = 0; ks < a.ksplit; ++ks) s += a.part_c[(int64_t)ks * a.part_c_ks + (int64_t)tok * nc + e];
-    a.q_c[(int64_t)tok * nc + e] = s;
+// Query prologue finish, one thread per element: the first ceil(T n_h d_h / 256)
+// workgroups sum the K-split partials of q^C into float32 scratch (the absorption
+// product's input), the others sum those of q^R_raw and rotate each interleaved pair by
+// its token's position (the partner element is in the neighbouring lane: n_h d_r is even,
+// so pairs never straddle a workgroup, a token or a head).
+__global__ __launch_bounds__(256) void query_finish(const QueryArgs a, int tokens, int c_blocks) {
+  const int64_t nc = (int64_t)tokens * a.n_h * a.d_h, nr = (int64_t)tokens * a.n_h * a.d_r;
+  if ((int)blockIdx.x < c_blocks) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= nc) return;
+    float v = 0.f;
+    for (int ks = 0; ks < a.ksplit; ++ks) v += a.part_c[(int64_t)ks * a.part_c_ks + e];
+    a.q_c[e] = v;
+    return;
   }
-  for (int e0 = 0; e0 < nr; e0 += 64) {                      // wave-uniform loop
-    const int e = e0 + lane;
-    float s = 0.f;
-    if (e < nr)
-      for (int ks = 0; ks < a.ksplit_r; ++ks) s += a.part_r[(int64_t)ks * a.part_r_ks + (int64_t)tok * nr + e];
-    const int within = e % a.d_r;                              // d_r even: pairs never straddle heads
-    const float r = rope_lane(s, within >> 1, a.d_r, pos, a.rope_base, (lane & 1) != 0);
-    if (e < nr) {
-      if (a.out_bf16) ((bf16*)a.q_pe)[(int64_t)tok * nr + e] = (bf16)r;
-      else ((float*)a.q_pe)[(int64_t)tok * nr + e] = r;
-    }
-  }
+  const int64_t e = (int64_t)(blockIdx.x - c_blocks) * 256 + threadIdx.x;
+  const bool in = e < nr;
+  const int64_t ec = in ? e : nr - 1;
+  const int per_tok = a.n_h * a.d_r;
+  const int tok = (int)(ec / per_tok);
+  const int within = (int)(ec - (int64_t)tok * per_tok) % a.d_r;
+  float v = 0.f;
+  if (in)
+    for (int ks = 0; ks < a.ksplit_r; ++ks) v += a.part_r[(int64_t)ks * a.part_r_ks + e];
+  const float r = rope_lane(v, within >> 1, a.d_r, a.positions[tok], a.rope_base, (threadIdx.x & 1) != 0);
+  if (!in) return;
+  if (a.out_bf16) ((bf16*)a.q_pe)[e] = (bf16)r;
+  else ((float*)a.q_pe)[e] = r;
 }
 
 // Sum of K-split partials [ksplit][n] into out (float32 or bf16), n elements.
@@ -269,11 +343,18 @@ __global__ __launch_bounds__(256) void transpose_heads(const T* src, T* dst, int
 
 hipError_t launch_gemm_nt(const GemmArgs& g, bool bf16_operands, int ksplit, hipStream_t s) {
   if (bf16_operands) {
-    dim3 grid((g.N + kTileN - 1) / kTileN, ksplit, g.batch * ((g.M + kTileM - 1) / kTileM));
-    if (g.a_f32)
-      hipLaunchKernelGGL(gemm_nt_bf16<true>, grid, dim3(64 * kGemmWaves), 0, s, g);
-    else
-      hipLaunchKernelGGL(gemm_nt_bf16<false>, grid, dim3(64 * kGemmWaves), 0, s, g);
+    const int mb = gemm_row_blocks(g.M);
+    const int nb = gemm_col_blocks(g.a_f32 != 0);
+    dim3 grid((g.N + 32 * nb * kGemmWaves - 1) / (32 * nb * kGemmWaves), ksplit,
+              g.batch * ((g.M + 32 * mb - 1) / (32 * mb)));
+    dim3 block(64 * kGemmWaves);
+    if (g.a_f32) {
+      if (mb == 2) hipLaunchKernelGGL((gemm_stream<2, 2, true, 8>), grid, block, 0, s, g);
+      else hipLaunchKernelGGL((gemm_stream<2, 1, true, 8>), grid, block, 0, s, g);
+    } else {
+      if (mb == 2) hipLaunchKernelGGL((gemm_stream<1, 2, false, 8>), grid, block, 0, s, g);
+      else hipLaunchKernelGGL((gemm_stream<1, 1, false, 8>), grid, block, 0, s, g);
+    }
   } else {
     dim3 grid((g.N + 63) / 64, ksplit, g.batch * ((g.M + 3) / 4));
     hipLaunchKernelGGL(gemm_nt_f32, grid, dim3(256), 0, s, g);
@@ -287,7 +368,9 @@ hipError_t launch_cache_write_finish(const CacheWriteArgs& a, int tokens, hipStr
 }
 
 hipError_t launch_query_finish(const QueryArgs& a, int tokens, hipStream_t s) {
-  hipLaunchKernelGGL(query_finish, dim3(tokens), dim3(64), 0, s, a);
+  const int64_t nc = (int64_t)tokens * a.n_h * a.d_h, nr = (int64_t)tokens * a.n_h * a.d_r;
+  const int c_blocks = (int)((nc + 255) / 256), r_blocks = (int)((nr + 255) / 256);
+  hipLaunchKernelGGL(query_finish, dim3(c_blocks + r_blocks), dim3(256), 0, s, a, tokens, c_blocks);
   return hipGetLastError();
 }
 

@@ -18,19 +18,22 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 mla_status_t status_of(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// K split of C[M, N] = A[M, K] B[N, K]^T: bf16 operands aim at >= 256 workgroups of 64 x 64
-// outputs with chunks of at least 128 (a multiple of 32); float32 operands use one chunk.
+// K split of C[M, N] = A[M, K] B[N, K]^T.  bf16 weights: about four waves of the
+// weight-streaming kernel per compute unit (1024 waves, each a block of 32 or 64 rows of B
+// times a row tile of A), with chunks of at least 256 (a multiple of 16); float32 operands
+// use one chunk.
 struct Split {
   int ksplit, kchunk;
 };
-Split split_of(long long M, long long N, int K, bool bf16) {
+Split split_of(long long M, long long N, int K, bool bf16, bool a_f32 = false) {
   if (!bf16) return {1, K};
-  const long long tiles = (long long)cdiv(N, 64) * cdiv(M, 64);
-  long long ks = (256 + tiles - 1) / tiles;
-  const long long max_ks = K / 128 > 0 ? K / 128 : 1;
+  const int rows = 32 * mla::gemm_row_blocks(M > INT_MAX ? INT_MAX : (int)M);
+  const long long waves = (long long)cdiv(N, 32 * mla::gemm_col_blocks(a_f32)) * cdiv(M, rows);
+  long long ks = (1024 + waves - 1) / waves;
+  const long long max_ks = K / 256 > 0 ? K / 256 : 1;
   if (ks > max_ks) ks = max_ks;
   if (ks < 1) ks = 1;
-  const int kchunk = cdiv(cdiv(K, ks), 32) * 32;
+  const int kchunk = cdiv(cdiv(K, ks), 16) * 16;
   return {cdiv(K, kchunk), kchunk};
 }
 
@@ -61,7 +64,7 @@ bool is_in_dtype(mla_dtype_t t) { return t == MLA_DTYPE_BF16 || t == MLA_DTYPE_F
 
 struct CacheWriteLayout {
   Split sp;
-  size_t bytes;
+  size_t rows, bytes;   // K-split partials [ksplit][T][d_c + d_r] at 0, summed rows at `rows`
 };
 
 mla_status_t check_cache_write(const mla_decode_params_t* p, int32_t d_model, int32_t s_new, CacheWriteLayout& l) {
@@ -78,7 +81,8 @@ mla_status_t check_cache_write(const mla_decode_params_t* p, int32_t d_model, in
   if (bf16 && (d_model % 32 || p->d_c % 16 || p->d_r % 16)) return MLA_ERR_SHAPE;
   const long long T = (long long)p->batch * s_new;
   l.sp = split_of(T, p->d_c + p->d_r, d_model, bf16);
-  l.bytes = a256((size_t)l.sp.ksplit * T * (p->d_c + p->d_r) * sizeof(float));
+  l.rows = a256((size_t)l.sp.ksplit * T * (p->d_c + p->d_r) * sizeof(float));
+  l.bytes = l.rows + a256((size_t)T * (p->d_c + p->d_r) * sizeof(float));
   return MLA_OK;
 }
 
@@ -122,7 +126,7 @@ mla_status_t check_output(const mla_decode_params_t* p, int32_t d_model, int32_t
   if (!bf16 && x_dtype != MLA_DTYPE_F32) return MLA_ERR_DTYPE;
   if (bf16 && (width % 32 || d_model % 16)) return MLA_ERR_SHAPE;
   const long long M = (long long)p->batch * p->s_q;
-  sp = split_of(M, d_model, width, bf16);
+  sp = split_of(M, d_model, width, bf16, x_dtype == MLA_DTYPE_F32);
   bytes = a256((size_t)sp.ksplit * M * d_model * sizeof(float));
   return MLA_OK;
 }
@@ -168,10 +172,11 @@ mla_status_t mla_cache_write(const mla_decode_params_t* params, int32_t d_model,
     st = status_of(mla::launch_gemm_nt(g, bf16, l.sp.ksplit, s));
     if (st != MLA_OK) return st;
   }
+  float* rows = (float*)((char*)workspace + l.rows);
+  st = status_of(mla::launch_sum_partials(part, part_ks, l.sp.ksplit, part_ks, rows, false, s));
+  if (st != MLA_OK) return st;
   mla::CacheWriteArgs a;
-  a.part = part;
-  a.part_ks = part_ks;
-  a.ksplit = l.sp.ksplit;
+  a.part = rows;
   a.d_c = p.d_c;
   a.d_r = p.d_r;
   a.s_new = s_new;
