@@ -605,9 +605,18 @@ def main():
         counted["measured_peaks"] = peaks
         counted["frac_of_measured_hbm"] = round(attn_gbs / peaks["hbm_read_gbs"], 4)
         counted["mfma_frac_of_measured"] = round(attn_tflops / peaks["bf16_mfma_tflops"], 4)
-    roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+    # The kernel's bound: HBM if its algorithmic intensity is below the machine's ridge (bf16 peak /
+    # HBM peak, 314.6 flop/B), else the bf16 matrix unit (s_q = 2, or an E4M3 cache's half bytes).
+    mfma_bound = alg["attn_flops"] / alg["attn_bytes"] > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        bound = {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4)}
+    else:
+        bound = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
+    roof = {**bound, "traffic": traffic,
             "kernel": kname, "kernel_us": round(attn_ms * 1e3, 2),
+            "hbm_gbs": round(attn_gbs, 1), "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4),
             "mfma_tflops": round(attn_tflops, 1), "mfma_frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
             "algorithmic_bytes_per_launch": alg["attn_bytes"], "algorithmic_flops_per_launch": alg["attn_flops"],
             **counted}
