@@ -292,6 +292,11 @@ void attn_partial_h128(const AttnParams p) {
       buffer_to_lds16(qp, r * (kDr * 2) + 16u * ((lz & 7u) ^ ((r >> 1) & 7u)), 0u, (unsigned char*)sm.p + wave * 4096 + j * 1024);
     }
   }
+  // The guessed block-table window has to land before its first lookup; waiting for it
+  // here (its load precedes the query copies, so this waits for that load alone, while the
+  // split walk waits for the lengths anyway) means no later lookup waits for it, and such a
+  // wait, placed by the compiler at the first lookup, also waited for the copies in flight.
+  pw.settle();
   bool first_piece = true;
 
   // Fused append, pool write of new row i of sequence w (row group 0) by wave
@@ -322,6 +327,7 @@ void attn_partial_h128(const AttnParams p) {
     const size_t row_base = ((size_t)pc.slot * p.s_q + q_pos) * p.n_h + head_base;
     if (pc.b != pw_b) {
       pw.init(p.block_table + (size_t)pc.b * p.max_pages, p.max_pages, p.num_pages, t0 / p.page_size);
+      pw.settle();
       pw_b = pc.b;
     }
     // Fused append: the tile (npt) and tile row (nrow) of each new row of this sequence
@@ -506,13 +512,23 @@ void attn_partial_h128(const AttnParams p) {
         // previous piece's staged u (not valid E4M3 codes).  Within the piece the ring
         // only holds cache rows or zeros.  (The first iteration's barrier orders these
         // writes before those reads.)
-        for (int i = threadIdx.x; i < LT::kVTile / 16; i += 64 * kWaves)
-          ((u32x4*)sm.v[kVRing - 1])[i] = u32x4{0u, 0u, 0u, 0u};
+        // (Addresses and the zero vector are made here from opaque values: kept from the
+        // kernel's start they were spilled to scratch and reloaded one memory round trip
+        // at a time.)
+        const uint32_t t = lane_id_opaque() + 64u * (uint32_t)wave;
+        const uint32_t z = opaque_zero();
+        unsigned char* slot3 = sm.v[kVRing - 1];
+#pragma unroll
+        for (int j = 0; j < LT::kVTile / (16 * 64 * kWaves); ++j)
+          *(u32x4*)(slot3 + 16u * (t + 64u * kWaves * j)) = u32x4{z, z, z, z};
       }
       // Zero probabilities of "tile -1" (buffer 1), this wave's head block.
+      {
+        const uint32_t z = opaque_zero();
+        unsigned char* pz = sm.p[1] + wave * 2 * 1024 + 16 * lane_id_opaque();
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
-        *(u32x4*)(sm.p[1] + (wave * 2 + half) * 1024 + 16 * lane_id_opaque()) = u32x4{0u, 0u, 0u, 0u};
+        for (int half = 0; half < 2; ++half) *(u32x4*)(pz + half * 1024) = u32x4{z, z, z, z};
+      }
       // No drain of older loads here: a wave's copies land in issue order and each wave
       // writes only its own ring rows, so an earlier pass's copies cannot overwrite
       // this pass's; the query loads are covered by the first iteration's wait.
@@ -525,6 +541,13 @@ void attn_partial_h128(const AttnParams p) {
       // not queue behind 36 query loads.
       uint32_t ready = 0;
       const uint32_t lz0 = lane_id_opaque();
+      // The first two tiles are described (page lookups, scalar work) before any copy of
+      // this pass is issued: a lookup may wait for the block-table window, and such a wait
+      // counts every vector-memory operation issued before it.
+      bool ok0, ok1;
+      const TileCopy tc0 = prepare_next(0 < ntiles, ok0);
+      const TileCopy tc1 = prepare_next(1 < ntiles, ok1);
+      ready |= (ok0 ? 1u : 0u) | (ok1 ? 2u : 0u);
       if (first_pass && fused) {
         // New row i goes to the stash, copied by wave i (before tile 0's copies, so the
         // first iteration's wait covers it; the first barrier makes it visible).
@@ -539,14 +562,10 @@ void attn_partial_h128(const AttnParams p) {
           }
       }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        bool ok;
-        const TileCopy tc = prepare_next(t < ntiles, ok);
-        ready |= ok ? (1u << t) : 0u;
+      for (int j = 0; j < LT::kCopies; ++j) copy_row(tc0, j, lz0);
+      if (first_pass && !(first_piece && pc.b == b_guess)) load_queries();
 #pragma unroll
-        for (int j = 0; j < LT::kCopies; ++j) copy_row(tc, j, lz0);
-        if (t == 0 && first_pass && !(first_piece && pc.b == b_guess)) load_queries();
-      }
+      for (int j = 0; j < LT::kCopies; ++j) copy_row(tc1, j, lz0);
       int vs = 0, ks3 = 0;   // ring slots of tile `it`
       for (int it = 0; it <= ntiles; ++it) {
         wait_copies();             // this wave's copies of tile `it` have landed, it+1's in flight

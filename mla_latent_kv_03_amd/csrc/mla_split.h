@@ -19,6 +19,7 @@ struct Piece {
   int t1;     // one past the last token (<= L_b)
   int slot;   // partial slot = share + b
   int len;    // L_b (clamped)
+  bool last;  // the share ends within this sequence: no later piece (set by for_each_piece_wave)
 };
 
 struct SplitScratch {
@@ -171,27 +172,34 @@ __device__ __forceinline__ unsigned long long udiv_mostly32(unsigned long long a
 // The pieces are found one at a time: each search rescans the lengths and returns the
 // first piece after a scalar cursor, so that no per-lane state of the scan stays live
 // while process() runs (a kernel's main loop then has the vector registers to itself).
+// A piece whose sequence reaches the share's end is the share's last: no search follows
+// it (one piece per share is the common case).
 template <class F>
 __device__ void for_each_piece_wave(const int32_t* __restrict__ seq_lens, int B, int max_tokens, int G, int w,
                                     int32_t* __restrict__ table, int len0, F&& process) {
   const int lane = threadIdx.x & 63;
-  auto len_of = [&](int base) {
+  // Lengths of sequences base .. base + 63.  The first search takes sequences 0..63 from
+  // len0 (loaded at kernel entry), so that for batches of up to 64 it loads nothing and
+  // waits for nothing (a wait for a vector load also waits for the caller's copies issued
+  // before it).  Every other block, and every later search, loads its lengths where they
+  // are used: len0 and what derives from it are then not live across process() (they were
+  // spilled, and the reloads' waits also waited for the copies and stores in flight).
+  auto len_of = [&](int base, bool from_len0) {
     const int b = base + lane;
-    const int raw = base == 0 ? len0 : seq_lens[b < B ? b : B - 1];
+    const int raw = from_len0 ? len0 : seq_lens[b < B ? b : B - 1];
     return b < B ? clamp_len(raw, max_tokens) : 0;
   };
   auto wave_sum = [](unsigned incl) { return (unsigned)__builtin_amdgcn_readlane((int)incl, 63); };
-  unsigned long long total = 0;
-  for (int base = 0; base < B; base += 64) total += wave_sum(wave_inclusive_scan_u32(units_of(len_of(base))));
+  unsigned long long total = wave_sum(wave_inclusive_scan_u32(units_of(len_of(0, true))));
+  for (int base = 64; base < B; base += 64) total += wave_sum(wave_inclusive_scan_u32(units_of(len_of(base, false))));
   const unsigned long long share = total > 0 ? udiv_mostly32(total - 1, (unsigned)G) + 1 : 1;
   const unsigned long long lo = (unsigned long long)w * share;
   const unsigned long long hi = lo + share < total ? lo + share : total;
 
   if (table) {
-    unsigned long long carry = 0;
-    for (int base = 0; base < B; base += 64) {
+    auto table_block = [&](int base, bool from_len0, unsigned long long& carry) {
       const int b = base + lane;
-      const unsigned n = units_of(len_of(base));
+      const unsigned n = units_of(len_of(base, from_len0));
       const unsigned incl = wave_inclusive_scan_u32(n);
       const unsigned long long start = carry + (incl - n);
       if (b < B && (unsigned)b % (unsigned)G == (unsigned)w) {
@@ -205,40 +213,52 @@ __device__ void for_each_piece_wave(const int32_t* __restrict__ seq_lens, int B,
         table[2 * b + 1] = cnt;
       }
       carry += wave_sum(incl);
-    }
+    };
+    unsigned long long carry = 0;
+    table_block(0, true, carry);
+    for (int base = 64; base < B; base += 64) table_block(base, false, carry);
   }
   if (total == 0) return;
 
-  // First piece of share w in a sequence after `after`; false if there is none.
-  auto next_piece = [&](int after, Piece& pc) {
-    unsigned long long carry = 0;
-    for (int base = 0; base < B; base += 64) {
-      const int b = base + lane;
-      const int L = len_of(base);
-      const unsigned n = units_of(L);
-      const unsigned incl = wave_inclusive_scan_u32(n);
-      const unsigned long long start = carry + (incl - n);
-      const bool mine = b > after && n > 0 && start < hi && start + n > lo;
-      const unsigned long long mask = __ballot(mine);
-      if (mask) {
-        const int src = __builtin_ctzll(mask);
-        const unsigned u0 = (unsigned)((lo > start ? lo : start) - start);
-        const unsigned u1 = (unsigned)((hi < start + n ? hi : start + n) - start);
-        const unsigned long long e = (unsigned long long)u1 * kSplitUnit;
-        pc.b = base + src;
-        pc.t0 = __builtin_amdgcn_readlane((int)(u0 * kSplitUnit), src);
-        pc.t1 = __builtin_amdgcn_readlane(e < (unsigned long long)L ? (int)e : L, src);
-        pc.len = __builtin_amdgcn_readlane(L, src);
-        pc.slot = w + pc.b;
-        return true;
-      }
-      carry += wave_sum(incl);
-      if (carry >= hi) break;
+  // Looks for the share's first piece in sequences base .. base + 63 after `after`:
+  // 1 = found (pc filled), 2 = the share ends before the next block, 0 = go on.
+  auto try_block = [&](int base, bool from_len0, int after, unsigned long long& carry, Piece& pc) -> int {
+    const int b = base + lane;
+    const int L = len_of(base, from_len0);
+    const unsigned n = units_of(L);
+    const unsigned incl = wave_inclusive_scan_u32(n);
+    const unsigned long long start = carry + (incl - n);
+    const bool mine = b > after && n > 0 && start < hi && start + n > lo;
+    const unsigned long long mask = __ballot(mine);
+    if (mask) {
+      const int src = __builtin_ctzll(mask);
+      const unsigned u0 = (unsigned)((lo > start ? lo : start) - start);
+      const unsigned u1 = (unsigned)((hi < start + n ? hi : start + n) - start);
+      const unsigned long long e = (unsigned long long)u1 * kSplitUnit;
+      pc.b = base + src;
+      pc.t0 = __builtin_amdgcn_readlane((int)(u0 * kSplitUnit), src);
+      pc.t1 = __builtin_amdgcn_readlane(e < (unsigned long long)L ? (int)e : L, src);
+      pc.len = __builtin_amdgcn_readlane(L, src);
+      pc.slot = w + pc.b;
+      pc.last = __builtin_amdgcn_readlane(start + n >= hi ? 1 : 0, src) != 0;
+      return 1;
     }
-    return false;
+    carry += wave_sum(incl);
+    return carry >= hi ? 2 : 0;
+  };
+  // First piece of share w in a sequence after `after`; false if there is none.
+  auto next_piece = [&](int after, Piece& pc, bool first_search) {
+    unsigned long long carry = 0;
+    int r = try_block(0, first_search, after, carry, pc);
+    for (int base = 64; r == 0 && base < B; base += 64) r = try_block(base, false, after, carry, pc);
+    return r == 1;
   };
   Piece pc;
-  for (int after = -1; next_piece(after, pc); after = pc.b) process(pc);
+  if (!next_piece(-1, pc, true)) return;
+  for (;;) {
+    process(pc);
+    if (pc.last || !next_piece(pc.b, pc, false)) break;
+  }
 }
 
 // Block-table entries of one sequence held in registers: lane j of the wave keeps the
