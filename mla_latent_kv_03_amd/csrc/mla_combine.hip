@@ -34,21 +34,24 @@ __device__ __forceinline__ int u_pos(int i, int k) { return i * kDc + ((((k >> 3
 // bf16 weights: one workgroup per (head, RB rows).
 //  Phase 1 merges the u of the RB rows.  A unit is (row, half row): lane l of the
 //  wave that owns it holds latent columns 256 h + 4 l .. +3.  With RB >= 4 each wave
-//  owns M = RB / 4 units, handled in a rolled loop that keeps the loads of the next
-//  unit in flight while it merges the current one; with RB < 4 the P = 8 / (2 RB)
-//  waves of a unit take every P-th slot and their sums are added in a fixed order
-//  through LDS.  A unit's slot lse values are loaded one slot per lane and read back as
-//  wave-uniform values for the merge weights; partial slices are read once, with the
-//  streaming (non-temporal) policy.  u enters the product as a bf16 high part plus a
-//  bf16 remainder (about 16 significant bits).
+//  owns M = RB / 4 units; with RB < 4 the P = 8 / (2 RB) waves of a unit take every
+//  P-th slot and their sums are added in a fixed order through LDS.  Every load of the
+//  workgroup is issued before the first merge: the W^UV_i rows of phase 2 (their
+//  addresses need nothing loaded), then, once the split table has come through the
+//  scalar cache, the slot lse values (one slot per lane) and the first kS partial slices
+//  of every unit (M kS = 32 per wave; slots past a unit's count re-read its last slot and
+//  get weight 0).  So the whole working set of a workgroup is in flight at once and the
+//  merge only waits for its own data.  Partial slices are read with the streaming
+//  (non-temporal) policy.  u enters the product as a bf16 high part plus a bf16
+//  remainder (about 16 significant bits).
 //  Phase 2: O[RB x 128] = U W^UV_i^T on 16x16x32 MFMAs; wave w owns output columns
-//  16 w .. 16 w + 15, whose W^UV_i rows it loads into registers during phase 1.
+//  16 w .. 16 w + 15.
 template <int RB>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const CombineParams p) {
   constexpr int kUnits = 2 * RB;
   constexpr int P = kUnits >= kCombineWaves ? 1 : kCombineWaves / kUnits;   // waves per unit
   constexpr int M = kUnits >= kCombineWaves ? kUnits / kCombineWaves : 1;   // units per wave
-  constexpr int kS = M == 1 ? 8 : 4;                                          // slices per load batch
+  constexpr int kS = 32 / M;                                                  // slices per unit in flight
   constexpr int kTileRows = RB < 16 ? 16 : RB;
   __shared__ __attribute__((aligned(16))) bf16 u_hi[kTileRows * kDc];
   __shared__ __attribute__((aligned(16))) bf16 u_lo[kTileRows * kDc];
@@ -63,91 +66,155 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const 
   const int part = wave % P;
   const size_t step = (size_t)p.s_q * p.n_h;                 // partial rows per slot
   const size_t slot_bytes = step * kDc * sizeof(bf16);
-  auto unit_of = [&](int m) { return P > 1 ? wave / P : wave + kCombineWaves * m; };
 
-  // Split-table entries of this wave's units: lane m holds unit m's (first, count).
-  int t_first = 0, t_count = 0;
-  if (lane < M) {
-    const int i = unit_of(lane) >> 1;
-    if (i < nrows) {
-      const int b = (row0 + i) / p.s_q;
-      t_first = p.split_table[2 * b];
-      t_count = p.split_table[2 * b + 1];
+  bf16x8 bw[kDc / 32];
+  if (p.w_uv) {
+    const bf16* wrow = (const bf16*)p.w_uv + ((size_t)head * kDv + 16 * wave + l16) * kDc + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < kDc / 32; ++kk) bw[kk] = *(const bf16x8*)(wrow + kk * 32);
+  }
+
+  // Units of this wave: m-th unit u = wave / P (P > 1) or wave + 8 m; row u / 2, half u % 2.
+  // The split-table entries are loaded unconditionally (rows past the block clamp to the
+  // last sequence) and checked afterwards, so that the scalar loads of all units are in
+  // flight together.
+  int u_row[M], u_half[M], u_cnt[M], u_first[M];
+  size_t u_base[M];   // partial row of the unit's first slot
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int u = P > 1 ? wave / P : wave + kCombineWaves * m;
+    u_row[m] = u >> 1;
+    u_half[m] = u & 1;
+    const int b = min((row0 + u_row[m]) / p.s_q, p.batch - 1);
+    u_first[m] = load_scalar(p.split_table + 2 * b);
+    u_cnt[m] = load_scalar(p.split_table + 2 * b + 1);
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    int first = u_first[m], count = u_cnt[m];
+    const bool bad = u_row[m] >= nrows || first < 0 || first >= p.num_slots || count <= 0;
+    first = bad ? 0 : first;                                  // slots clipped to the pool
+    count = bad ? 0 : min(count, p.num_slots - first);
+    u_cnt[m] = count;
+    u_base[m] = ((size_t)first * p.s_q + (row0 + u_row[m]) % p.s_q) * p.n_h + head;
+  }
+  // Merge layout: lane (vm, vs) = (lane / L, lane % L) holds slot vs of unit vm, so one
+  // load brings the slot lse values of all the wave's units and the maximum and the sum
+  // are segmented lane reductions.  A unit with more than L slots sends the wave to the
+  // per-unit merge below.
+  constexpr int L = 64 / M;
+  const int vm = lane / L, vs = lane % L;
+  int v_cnt = u_cnt[0], v_row = u_row[0], v_half = u_half[0];
+  size_t v_base = u_base[0];
+#pragma unroll
+  for (int m = 1; m < M; ++m)
+    if (vm == m) { v_cnt = u_cnt[m]; v_row = u_row[m]; v_half = u_half[m]; v_base = u_base[m]; }
+  bool all_fit = true;
+#pragma unroll
+  for (int m = 0; m < M; ++m) all_fit = all_fit && u_cnt[m] <= L;
+  const float v_l = vs < v_cnt ? p.part_lse[v_base + vs * step] : -INFINITY;
+  bf16x4 u_v[M][kS];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const char* src = (const char*)((const bf16*)p.part_u + u_base[m] * kDc + 256 * u_half[m]) + 8 * lane;
+    const int last = u_cnt[m] > 0 ? u_cnt[m] - 1 : 0;
+#pragma unroll
+    for (int k = 0; k < kS; ++k) {
+      const int s = min(part + P * k, last);
+      u_v[m][k] = __builtin_nontemporal_load((const bf16x4*)(src + (size_t)s * slot_bytes));
     }
   }
 
-  // Loads of one unit in flight: its slot lse values (slot = lane) and the first kS of
-  // its slices (slot part + P k).
-  struct Unit {
-    int row, half, cnt;
-    size_t base;   // partial row of the unit's first slot
-    float l;
-    bf16x4 v[kS];
-  };
-  auto start = [&](int m, Unit& st) {
-    const int u = unit_of(m);
-    st.row = u >> 1;
-    st.half = u & 1;
-    int first = __builtin_amdgcn_readlane(t_first, m);
-    int count = __builtin_amdgcn_readlane(t_count, m);
-    if (first < 0 || first >= p.num_slots || count <= 0) { first = 0; count = 0; }   // slots clipped to the pool
-    if (count > p.num_slots - first) count = p.num_slots - first;
-    st.cnt = st.row < nrows ? count : 0;
-    st.base = ((size_t)first * p.s_q + (row0 + st.row) % p.s_q) * p.n_h + head;
-    st.l = lane < st.cnt ? p.part_lse[st.base + lane * step] : -INFINITY;
-    const char* src = (const char*)((const bf16*)p.part_u + st.base * kDc + 256 * st.half) + 8 * lane;
+  // Weights w = exp(lse_s - lse) of the merge layout's slots (all units at once).
+  float v_w = 0.f;
+  if (all_fit) {
+    float x = v_l;
+#pragma unroll
+    for (int o = L / 2; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    const float e = v_l == -INFINITY ? 0.f : exp2_fast((v_l - x) * kLog2e);
+    float tot = e;
+#pragma unroll
+    for (int o = L / 2; o >= 1; o >>= 1) tot += __shfl_xor(tot, o, 64);
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    if (p.lse && vs == 0 && v_half == 0 && part == 0 && v_row < nrows)
+      p.lse[(size_t)(row0 + v_row) * p.n_h + head] = tot > 0.f ? x + logf(tot) : -INFINITY;
+    v_w = e * inv;
+  }
+  // u of unit m: its slices weighted by the merge layout's weights (lane L m + slot).
+  auto accumulate = [&](int m) {
+    const int cnt = u_cnt[m];
+    auto weight = [&](int s) -> float { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_w), L * m + s)); };
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kS; ++k) {
       const int s = part + P * k;
-      if (s < st.cnt) st.v[k] = __builtin_nontemporal_load((const bf16x4*)(src + (size_t)s * slot_bytes));
+      if (s < cnt) acc += weight(s) * from_bf16x4(u_v[m][k]);
     }
+    // Slots past the first kS of this wave (at most L in all): further batches of kS loads.
+    const char* src = (const char*)((const bf16*)p.part_u + u_base[m] * kDc + 256 * u_half[m]) + 8 * lane;
+    for (int j0 = kS; part + P * j0 < cnt; j0 += kS) {
+      bf16x4 v[kS];
+#pragma unroll
+      for (int k = 0; k < kS; ++k) {
+        const int s = min(part + P * (j0 + k), cnt - 1);
+        v[k] = __builtin_nontemporal_load((const bf16x4*)(src + (size_t)s * slot_bytes));
+      }
+#pragma unroll
+      for (int k = 0; k < kS; ++k) {
+        const int s = part + P * (j0 + k);
+        if (s < cnt) acc += weight(s) * from_bf16x4(v[k]);
+      }
+    }
+    return acc;
   };
-  // Merge one unit: weights w_s = exp(lse_s - lse) for slot = lane (64 at a time), the
-  // maximum and the sum over wave-uniform values read back lane by lane.
-  auto finish = [&](Unit& st) {
-    const int cnt = st.cnt;
+  // Per-unit merge (a unit with more than L slots): slot = lane, 64 at a time, the maximum
+  // and the sum over wave-uniform values read back lane by lane.
+  auto finish = [&](int m) {
+    const int cnt = u_cnt[m];
+    const size_t base = u_base[m];
+    const float l = lane < cnt ? p.part_lse[base + lane * step] : -INFINITY;
     const int c64 = min(cnt, 64);
     float x = -INFINITY;
-    for (int s = 0; s < c64; ++s) x = fmaxf(x, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(st.l), s)));
+    for (int s = 0; s < c64; ++s) x = fmaxf(x, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), s)));
     if (cnt > 64) {
       float y = x;
-      for (int s = 64 + lane; s < cnt; s += 64) y = fmaxf(y, p.part_lse[st.base + s * step]);
+      for (int s = 64 + lane; s < cnt; s += 64) y = fmaxf(y, p.part_lse[base + s * step]);
       x = wave_max(y);
     }
-    const float e = st.l == -INFINITY ? 0.f : exp2_fast((st.l - x) * kLog2e);
+    const float e = l == -INFINITY ? 0.f : exp2_fast((l - x) * kLog2e);
     float tot = 0.f;
     for (int s = 0; s < c64; ++s) tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), s));
     if (cnt > 64) {
       float t = 0.f;
       for (int s = 64 + lane; s < cnt; s += 64) {
-        const float l = p.part_lse[st.base + s * step];
-        if (l != -INFINITY) t += exp2_fast((l - x) * kLog2e);
+        const float ls = p.part_lse[base + s * step];
+        if (ls != -INFINITY) t += exp2_fast((ls - x) * kLog2e);
       }
       tot += wave_sum(t);
     }
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    if (p.lse && st.half == 0 && part == 0 && lane == 0 && st.row < nrows)
-      p.lse[(size_t)(row0 + st.row) * p.n_h + head] = tot > 0.f ? x + logf(tot) : -INFINITY;
+    if (p.lse && u_half[m] == 0 && part == 0 && lane == 0 && u_row[m] < nrows)
+      p.lse[(size_t)(row0 + u_row[m]) * p.n_h + head] = tot > 0.f ? x + logf(tot) : -INFINITY;
     const float w = e * inv;
     auto weight = [&](int s) -> float {
       if (s < 64) return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
-      const float l = p.part_lse[st.base + s * step];
-      return l == -INFINITY ? 0.f : exp2_fast((l - x) * kLog2e) * inv;
+      const float ls = p.part_lse[base + s * step];
+      return ls == -INFINITY ? 0.f : exp2_fast((ls - x) * kLog2e) * inv;
     };
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kS; ++k) {
       const int s = part + P * k;
-      if (s < cnt) acc += weight(s) * from_bf16x4(st.v[k]);
+      if (s < cnt) acc += weight(s) * from_bf16x4(u_v[m][k]);
     }
     // Slots past the first kS of this wave: further batches of kS loads.
-    const char* src = (const char*)((const bf16*)p.part_u + st.base * kDc + 256 * st.half) + 8 * lane;
+    const char* src = (const char*)((const bf16*)p.part_u + base * kDc + 256 * u_half[m]) + 8 * lane;
     for (int j0 = kS; part + P * j0 < cnt; j0 += kS) {
       bf16x4 v[kS];
 #pragma unroll
       for (int k = 0; k < kS; ++k) {
-        const int s = part + P * (j0 + k);
-        if (s < cnt) v[k] = __builtin_nontemporal_load((const bf16x4*)(src + (size_t)s * slot_bytes));
+        const int s = min(part + P * (j0 + k), cnt - 1);
+        v[k] = __builtin_nontemporal_load((const bf16x4*)(src + (size_t)s * slot_bytes));
       }
 #pragma unroll
       for (int k = 0; k < kS; ++k) {
@@ -176,35 +243,18 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const 
     *(bf16x4*)(u_lo + pos) = lo;
   };
 
-  Unit A, B;
-  start(0, A);
-  if (M > 1) start(1, B);
-  // W^UV_i rows for phase 2 after the first units' loads, which must not queue behind them.
-  bf16x8 bw[kDc / 32];
-  if (p.w_uv) {
-    const bf16* wrow = (const bf16*)p.w_uv + ((size_t)head * kDv + 16 * wave + l16) * kDc + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < kDc / 32; ++kk) bw[kk] = *(const bf16x8*)(wrow + kk * 32);
-  }
   if (P > 1) {
-    red[P > 1 ? wave : 0][lane] = finish(A);
+    red[P > 1 ? wave : 0][lane] = all_fit ? accumulate(0) : finish(0);
     __syncthreads();
     if (part == 0) {
       f32x4 a = red[P > 1 ? wave : 0][lane];
 #pragma unroll
       for (int k = 1; k < P; ++k) a += red[P > 1 ? wave + k : 0][lane];
-      store_u(A.row, A.half, a);
+      store_u(u_row[0], u_half[0], a);
     }
   } else {
-#pragma unroll 1
-    for (int m = 0; m < M; m += 2) {
-      store_u(A.row, A.half, finish(A));
-      if (m + 2 < M) start(m + 2, A);
-      if (m + 1 < M) {
-        store_u(B.row, B.half, finish(B));
-        if (m + 3 < M) start(m + 3, B);
-      }
-    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) store_u(u_row[m], u_half[m], all_fit ? accumulate(m) : finish(m));
   }
   __syncthreads();
   if (!p.w_uv) return;   // kernel-uniform
