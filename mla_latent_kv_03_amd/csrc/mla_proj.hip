@@ -21,30 +21,66 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kGemmWaves = 4;
 
+// The buffer->LDS copy of buffer_to_lds16 with the default cache policy (the activation
+// rows are read by every workgroup).
+__device__ __forceinline__ void buffer_to_lds16_cached(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t soffset,
+                                                       void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(lds_wave_base), 16, voffset, soffset, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) alone (lgkmcnt and expcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void gemm_wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+constexpr int kGemmRing = 12;      // k-steps in flight (bf16 A: 80 KiB of LDS, two workgroups per CU)
+constexpr int kGemmRingF32 = 12;   // float32 A, two B blocks per wave: 160 KiB of LDS
+
 // C[M, N] (+)= A[M, K] B[N, K]^T for bf16 B (the weights) and bf16 or float32 A (the few
 // activation rows of a decode step), built to stream B from HBM once at full rate.
 //
 // A workgroup of four waves covers 4 NB blocks of 32 rows of B, a K chunk (blockIdx.y)
 // and a row tile of A (blockIdx.z: MB blocks of 32 rows, rows past M clamped to M - 1 and
-// never stored).  Per 16-wide k-step each wave loads 16 bytes of each of its B rows into
-// a register ring of D steps (loads run D steps ahead of their MFMAs) and issues NB x MB
-// 32x32x16 MFMAs, with A rows as the first operand and B rows as the second, so that lane
-// l ends up holding C[8(v/4) + 4(l/32) + v%4][l%32] and each 32-lane half stores 128
+// never stored).  Per 16-wide k-step a wave issues NB MFMAs per 32-row block of A
+// (32x32x16), with A rows as the first operand and B rows as the second, so that lane l
+// ends up holding C[8(v/4) + 4(l/32) + v%4][l%32] and each 32-lane half stores 128
 // contiguous bytes of a C row.
-// A is read from the caches once per workgroup, not once per wave (measured: every wave
-// re-reading its A fragments from the L2 held the B stream to about a third of the HBM
-// rate): blocks of 4 k-steps of A are staged in LDS in MFMA fragment order (fragment
-// (step, m-block) = 64 lanes x 16 bytes, float32 A: two such halves), three blocks deep;
-// each wave loads its share of block b + 2 into registers while block b is computed and
-// stores it after the next barrier, so one barrier per block orders everything.  Steps
-// past the chunk read the chunk's last B step and zero A, so whole rounds run unguarded.
+//
+// Both operands reach the MFMAs through LDS, in blocks of four k-steps (128 bytes of a
+// bf16 row, 256 of a float32 row), copied by buffer->LDS loads that read whole 128-byte
+// lines: a copy covers 8 rows x 128 bytes (float32 A: 4 rows x 256), lane l taking
+// 16-byte chunk (l % 8) ^ (row % 8) of its row (l % 16 for 256-byte rows), so that chunk c
+// of row r sits at position c ^ (r % 8) of the row in LDS and the operand reads (16 rows,
+// one chunk each) hit distinct banks.  Copies that read 32 bytes of 32 different lines
+// each held the weight stream to about 3.3 TB/s; whole lines per copy are what a plain
+// streaming read needs for full rate.  Copies carry no register results, so their waits
+// are exact counts written here (register loads into a ring made the compiler drain the
+// ring at every loop head).
+//  - B: each wave streams its own rows through a private ring of RA = D / 4 blocks; block
+//    b + RA is copied at the end of block b, into the slot block b has left.
+//  - A: RA + 1 shared slots; block b + RA is copied at the start of block b (into the slot
+//    of block b - 1, which every wave has finished at the barrier), each wave a quarter
+//    of its rows; one barrier per block publishes it.
+// Per wave the copies go out in a fixed order (block b: A(b + RA), then B(b + RA)), so
+// the number issued after any copy is a constant.  The resources end at the operands' last
+// bytes, so reads past them return zeros.  RAGGED: a chunk may end inside a block (K or
+// the chunk not a multiple of 64), whose steps past the chunk are skipped; otherwise every
+// block is whole and its operands are read from LDS before its MFMAs.
 // AF32: A enters as a bf16 high part plus a bf16 remainder (two MFMAs per pair).
-template <int NB, int MB, bool AF32, int D>
+template <int NB, int MB, bool AF32, int D, bool RAGGED>
 __global__ __launch_bounds__(64 * kGemmWaves) void gemm_stream(const GemmArgs g) {
-  static_assert(D == 8, "the round is two A blocks of four steps");
-  constexpr int kFrag = 1024 * (AF32 ? 2 : 1);   // bytes of one A fragment
-  constexpr int kSlot = 4 * MB * kFrag;          // one A block
-  __shared__ __attribute__((aligned(16))) unsigned char a_lds[3 * kSlot];
+  static_assert(D % 4 == 0 && D >= 8, "the ring holds whole blocks of four steps");
+  constexpr int RA = D / 4;                          // blocks in flight
+  constexpr int SA = RA + 1;                         // A slots
+  constexpr int kAElem = AF32 ? 4 : 2;
+  constexpr int kARow = 64 * kAElem;                 // bytes of an A row in one block
+  constexpr int kASlot = 32 * MB * kARow;            // one A block
+  constexpr int kBBlock = 32 * NB * 128;             // one block of one wave's B rows
+  constexpr int kACopies = kASlot / 1024 / kGemmWaves;
+  constexpr int kBCopies = kBBlock / 1024;
+  constexpr int kWait = (RA - 1) * (kACopies + kBCopies);
+  static_assert(kWait < 64, "vmcnt holds 6 bits");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[SA * kASlot + kGemmWaves * RA * kBBlock];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, kh = lane >> 5;
@@ -56,47 +92,45 @@ __global__ __launch_bounds__(64 * kGemmWaves) void gemm_stream(const GemmArgs g)
   const int k0 = blockIdx.y * g.kchunk;
   const int k1 = min(g.K, k0 + g.kchunk);
   const int nsteps = (k1 - k0) >> 4;
-  if (nsteps <= 0) return;                       // workgroup-uniform
-  const int nrounds = (nsteps + 7) >> 3;
-  const bf16* bp[NB];
+  if (nsteps <= 0) return;                           // workgroup-uniform
+  const int nblocks = (nsteps + 3) >> 2;
+
+  // B copy i of a block: rows 8 i .. 8 i + 7 of the wave's 32 NB rows.
+  const int64_t b_bytes = ((int64_t)(g.N - 1) * g.ldb + g.K) * 2;
+  const __amdgpu_buffer_rsrc_t rs_b = buffer_rsrc((const bf16*)g.b + bt * g.b_bs, (int)min(b_bytes, (int64_t)INT32_MAX));
+  uint32_t vo_b[kBCopies];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-    bp[nb] = (const bf16*)g.b + bt * g.b_bs + (int64_t)min(n0 + 32 * nb + l32, g.N - 1) * g.ldb + k0 + 8 * kh;
-  // This wave's A fragments of every block: f = wave + 4 j (j < MB), step f / MB, m-block
-  // f % MB; arow[j] is the start of the fragment's A row.
-  int64_t arow[MB];
-#pragma unroll
-  for (int j = 0; j < MB; ++j) {
-    const int mb = (wave + 4 * j) % MB;
-    arow[j] = bt * g.a_bs + (int64_t)min(m0 + 32 * mb + l32, g.M - 1) * g.lda;
+  for (int i = 0; i < kBCopies; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    vo_b[i] = (uint32_t)((int64_t)min(n0 + r, g.N - 1) * g.ldb * 2) + 16u * (uint32_t)((lane & 7) ^ (r & 7));
   }
-  u32x4 ar[MB][AF32 ? 2 : 1];
-  auto load_a = [&](int blk) {
+  unsigned char* const bring = lds + SA * kASlot + wave * RA * kBBlock;
+  auto copy_b = [&](int blk) {
+    const uint32_t so = (uint32_t)(k0 + 64 * blk) * 2u;
+    unsigned char* dst = bring + (blk % RA) * kBBlock;
 #pragma unroll
-    for (int j = 0; j < MB; ++j) {
-      const int f = wave + 4 * j;
-      const int k = k0 + 64 * blk + 16 * (f / MB) + 8 * kh;   // 8 values; the chunk ends on a multiple of 16
-      const bool in = k < k1;
-      const int64_t off = arow[j] + (in ? k : k0);            // past the chunk: an in-bounds read, zeroed
-      if constexpr (AF32) {
-        const float* x = (const float*)g.a + off;
-        ar[j][0] = *(const u32x4*)x;
-        ar[j][AF32 ? 1 : 0] = *(const u32x4*)(x + 4);
-        if (!in) ar[j][0] = ar[j][AF32 ? 1 : 0] = u32x4{0u, 0u, 0u, 0u};
-      } else {
-        ar[j][0] = *(const u32x4*)((const bf16*)g.a + off);
-        if (!in) ar[j][0] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+    for (int i = 0; i < kBCopies; ++i) buffer_to_lds16_cached(rs_b, vo_b[i], so, dst + 1024 * i);
   };
-  auto store_a = [&](int slot) {
+  // A copy ii = wave + 4 j: rows 8 ii .. (float32: 4 ii ..) of the 32 MB rows.
+  constexpr int kARowsPerCopy = 1024 / kARow;
+  const int64_t a_bytes = ((int64_t)(g.M - 1) * g.lda + g.K) * kAElem;
+  const __amdgpu_buffer_rsrc_t rs_a =
+      buffer_rsrc((const unsigned char*)g.a + (int64_t)bt * g.a_bs * kAElem, (int)min(a_bytes, (int64_t)INT32_MAX));
+  uint32_t vo_a[kACopies];
 #pragma unroll
-    for (int j = 0; j < MB; ++j) {
-      unsigned char* dst = a_lds + slot * kSlot + (wave + 4 * j) * kFrag + 16 * lane;
-      *(u32x4*)dst = ar[j][0];
-      if constexpr (AF32) *(u32x4*)(dst + 1024) = ar[j][AF32 ? 1 : 0];
-    }
+  for (int j = 0; j < kACopies; ++j) {
+    const int ii = wave + kGemmWaves * j;
+    const int rr = kARowsPerCopy * ii + lane / (kARow / 16);
+    const int c = (lane % (kARow / 16)) ^ (rr & 7);
+    vo_a[j] = (uint32_t)((int64_t)min(m0 + rr, g.M - 1) * g.lda * kAElem) + 16u * (uint32_t)c;
+  }
+  auto copy_a = [&](int blk) {
+    const uint32_t so = (uint32_t)(k0 + 64 * blk) * (uint32_t)kAElem;
+    unsigned char* slot = lds + (blk % SA) * kASlot;
+#pragma unroll
+    for (int j = 0; j < kACopies; ++j) buffer_to_lds16_cached(rs_a, vo_a[j], so, slot + 1024 * (wave + kGemmWaves * j));
   };
+
   f32x16 acc[NB][MB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -104,19 +138,32 @@ __global__ __launch_bounds__(64 * kGemmWaves) void gemm_stream(const GemmArgs g)
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[nb][mb][v] = 0.f;
-  bf16x8 ring[D][NB];
-  auto load_w = [&](int step, bf16x8* w) {
-    const int k = 16 * min(step, nsteps - 1);
+  // Operand rows of this lane: B row 32 nb + l32 of the wave's block, A row 32 mb + l32.
+  const int sw = l32 & 7;                            // (32 x + l32) % 8
+  // Operands of step j (0..3) of block blk: B fragments w, A fragments a (float32 A: the
+  // two 16-byte halves of each).
+  constexpr int kAF = MB * (AF32 ? 2 : 1);
+  auto read_ops = [&](int blk, int j, bf16x8* w, u32x4* a) {
+    const unsigned char* bsrc = bring + (blk % RA) * kBBlock + 128 * l32 + 16 * ((2 * j + kh) ^ sw);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) w[nb] = *(const bf16x8*)(bp[nb] + k);
-  };
-  // Step j (0..3) of the block in `slot`, with B fragments w.
-  auto compute = [&](int slot, int j, const bf16x8* w) {
+    for (int nb = 0; nb < NB; ++nb) w[nb] = *(const bf16x8*)(bsrc + 4096 * nb);
+    const unsigned char* abase = lds + (blk % SA) * kASlot + kARow * l32;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const unsigned char* src = a_lds + slot * kSlot + (j * MB + mb) * kFrag + 16 * lane;
+      const unsigned char* arow = abase + 32 * kARow * mb;
       if constexpr (AF32) {
-        const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 1024);
+        a[2 * mb] = *(const u32x4*)(arow + 16 * ((4 * j + 2 * kh) ^ sw));
+        a[2 * mb + 1] = *(const u32x4*)(arow + 16 * ((4 * j + 2 * kh + 1) ^ sw));
+      } else {
+        a[mb] = *(const u32x4*)(arow + 16 * ((2 * j + kh) ^ sw));
+      }
+    }
+  };
+  auto mfmas = [&](const bf16x8* w, const u32x4* a) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if constexpr (AF32) {
+        const f32x4 x0 = (f32x4)a[2 * mb], x1 = (f32x4)a[2 * mb + 1];
         bf16x8 hi, lo;
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
@@ -132,40 +179,52 @@ __global__ __launch_bounds__(64 * kGemmWaves) void gemm_stream(const GemmArgs g)
           acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, w[nb], acc[nb][mb], 0, 0, 0);
         }
       } else {
-        const bf16x8 a = *(const bf16x8*)src;
+        const bf16x8 x = (bf16x8)a[mb];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w[nb], acc[nb][mb], 0, 0, 0);
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, w[nb], acc[nb][mb], 0, 0, 0);
       }
     }
   };
+  auto compute = [&](int blk, int j) {
+    bf16x8 w[NB];
+    u32x4 a[kAF];
+    read_ops(blk, j, w, a);
+    mfmas(w, a);
+  };
 
-  load_a(0);
-  store_a(0);
-  load_a(1);
 #pragma unroll
-  for (int j = 0; j < D; ++j) load_w(j, ring[j]);
-  for (int r = 0; r < nrounds; ++r) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int blk = 2 * r + h;
-      __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): this wave's A stores are done
-      __builtin_amdgcn_s_barrier();                // A(blk) is in LDS; block blk - 1 is finished
-      __builtin_amdgcn_sched_barrier(0);
-      store_a((blk + 1) % 3);
-      load_a(blk + 2);
-      const int slot = blk % 3;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // Keep the program order: the scheduler would otherwise sink the loads below the
-        // MFMAs and drain the ring once per round.
-        __builtin_amdgcn_sched_barrier(0);
-        compute(slot, j, ring[4 * h + j]);
-        load_w(8 * r + 4 * h + j + D, ring[4 * h + j]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int b = 0; b < RA; ++b) {
+    copy_a(b);
+    copy_b(b);
   }
+  for (int blk = 0; blk < nblocks; ++blk) {
+    gemm_wait_vmcnt<kWait>();                        // this wave's copies of A(blk) and B(blk) landed
+    __builtin_amdgcn_s_barrier();                    // all of A(blk); block blk - 1 finished everywhere
+    __builtin_amdgcn_sched_barrier(0);
+    copy_a(blk + RA);                                // into the slot of block blk - 1
+    if constexpr (RAGGED) {
+      for (int j = 0; j < 4 && 4 * blk + j < nsteps; ++j) compute(blk, j);
+    } else {
+      // All reads of the block first (two steps at a time for float32 A), then its MFMAs.
+      constexpr int kBatch = AF32 ? 2 : 4;
+#pragma unroll
+      for (int j0 = 0; j0 < 4; j0 += kBatch) {
+        bf16x8 w[kBatch][NB];
+        u32x4 a[kBatch][kAF];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) read_ops(blk, j0 + j, w[j], a[j]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) mfmas(w[j], a[j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): B(blk) has been read
+    __builtin_amdgcn_sched_barrier(0);
+    copy_b(blk + RA);                                // into the slot block blk has left
+  }
+  gemm_wait_vmcnt<0>();                              // no copy may land after the workgroup ends
   if (n0 >= g.N) return;
   // Lane holds C[m0 + 32 mb + 8 (v/4) + 4 kh + v%4][n0 + 32 nb + l32].
   const int64_t cbase = (int64_t)blockIdx.y * g.c_ks + bt * g.c_bs;
@@ -343,18 +402,44 @@ __global__ __launch_bounds__(256) void transpose_heads(const T* src, T* dst, int
 
 hipError_t launch_gemm_nt(const GemmArgs& g, bool bf16_operands, int ksplit, hipStream_t s) {
   if (bf16_operands) {
+    // The copies address B and A through 32-bit buffer offsets: a B of 2 GiB or more runs
+    // as several launches over row ranges of B (columns of C).
+    const int64_t max_bytes = (int64_t)1 << 31;
+    const int64_t a_bytes = ((int64_t)(g.M - 1) * g.lda + g.K) * (g.a_f32 ? 4 : 2);
+    if (a_bytes >= max_bytes) return hipErrorInvalidValue;
+    const int64_t b_bytes = ((int64_t)(g.N - 1) * g.ldb + g.K) * 2;
+    if (b_bytes >= max_bytes) {
+      const int rows = (int)((max_bytes / 2 - g.K) / g.ldb) & ~127;   // whole workgroups of B rows
+      if (rows < 128) return hipErrorInvalidValue;
+      for (int n = 0; n < g.N; n += rows) {
+        GemmArgs part = g;
+        part.b = (const bf16*)g.b + (int64_t)n * g.ldb;
+        part.c = g.out_bf16 ? (void*)((bf16*)g.c + n) : (void*)((float*)g.c + n);
+        part.N = min(rows, g.N - n);
+        const hipError_t e = launch_gemm_nt(part, true, ksplit, s);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
     const int mb = gemm_row_blocks(g.M);
     const int nb = gemm_col_blocks(g.a_f32 != 0);
     dim3 grid((g.N + 32 * nb * kGemmWaves - 1) / (32 * nb * kGemmWaves), ksplit,
               g.batch * ((g.M + 32 * mb - 1) / (32 * mb)));
     dim3 block(64 * kGemmWaves);
+    const bool ragged = g.K % 64 != 0 || g.kchunk % 64 != 0;
+#define MLA_GEMM(NB_, MB_, F32_, D_)                                                  \
+  do {                                                                             \
+    if (ragged) hipLaunchKernelGGL((gemm_stream<NB_, MB_, F32_, D_, true>), grid, block, 0, s, g);  \
+    else hipLaunchKernelGGL((gemm_stream<NB_, MB_, F32_, D_, false>), grid, block, 0, s, g);        \
+  } while (0)
     if (g.a_f32) {
-      if (mb == 2) hipLaunchKernelGGL((gemm_stream<2, 2, true, 8>), grid, block, 0, s, g);
-      else hipLaunchKernelGGL((gemm_stream<2, 1, true, 8>), grid, block, 0, s, g);
+      if (mb == 2) MLA_GEMM(2, 2, true, kGemmRingF32);
+      else MLA_GEMM(2, 1, true, kGemmRingF32);
     } else {
-      if (mb == 2) hipLaunchKernelGGL((gemm_stream<1, 2, false, 8>), grid, block, 0, s, g);
-      else hipLaunchKernelGGL((gemm_stream<1, 1, false, 8>), grid, block, 0, s, g);
+      if (mb == 2) MLA_GEMM(1, 2, false, kGemmRing);
+      else MLA_GEMM(1, 1, false, kGemmRing);
     }
+#undef MLA_GEMM
   } else {
     dim3 grid((g.N + 63) / 64, ksplit, g.batch * ((g.M + 3) / 4));
     hipLaunchKernelGGL(gemm_nt_f32, grid, dim3(256), 0, s, g);

@@ -33,7 +33,9 @@ Split split_of(long long M, long long N, int K, bool bf16, bool a_f32 = false) {
   const long long max_ks = K / 256 > 0 ? K / 256 : 1;
   if (ks > max_ks) ks = max_ks;
   if (ks < 1) ks = 1;
-  const int kchunk = cdiv(cdiv(K, ks), 16) * 16;
+  // Chunks of whole 64-wide blocks where K allows (the product kernel's fast path).
+  const int align = K % 64 == 0 ? 64 : 16;
+  const int kchunk = cdiv(cdiv(K, ks), align) * align;
   return {cdiv(K, kchunk), kchunk};
 }
 
