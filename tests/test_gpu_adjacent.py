@@ -192,6 +192,37 @@ def test_cache_write_v3_slice(kv):
     compare_sampled(case, out, lse, range(B), BF16_TOL, lse_tol=5e-3, what=f"cache_write v3 {kv} -> decode")
 
 
+@pytest.mark.parametrize("n_seq", [4, 20])
+def test_cache_write_ragged_k(n_seq):
+    """d_model 7200 (a multiple of 32, not of 64): the product's K chunks end inside a block of four
+    k-steps, so the kernel that skips the steps past a chunk runs; 8 and 40 new rows (one and
+    two 32-row tiles of A).  Every stored bf16 value against the oracle's cache rows."""
+    _case("cache_write ragged K", n_seq=n_seq)
+    from mla_latent_kv_03_amd import binding
+    d_model, s_new = 7200, 2
+    rng = np.random.default_rng(1250 + n_seq)
+    lens = rng.integers(70, 3000, size=n_seq)
+    x = workloads.make_decode(lens.tolist(), page_size=64, seed=1251 + n_seq, **workloads.V3)
+    w = workloads.layer_weights(1252 + n_seq, d_model=d_model, n_h=128, d_c=512, d_h=128, d_r=64, d_v=128,
+                                n_tokens=n_seq * s_new, with_o=False)
+    positions = np.stack([np.arange(L - s_new, L) for L in lens]).astype(np.int32)
+    case = DeviceCase(x)
+    h_bf = torch.from_numpy(w["h"]).to(torch.bfloat16)
+    wd, wk = (torch.from_numpy(w[k]).to(torch.bfloat16) for k in ("dkv", "kr"))
+    binding.mla_cache_write(case.params, h_bf.reshape(n_seq, s_new, d_model).cuda(), wd.cuda(), wk.cuda(),
+                            torch.from_numpy(positions).cuda(), case.block_table, case.c_kv, case.k_pe, case.kv_scale)
+    torch.cuda.synchronize()
+    c, k_r = ref.cache_rows(h_bf.double().numpy(), wd.double().numpy(), wk.double().numpy(), positions.reshape(-1))
+    exact = np.concatenate([c, k_r], 1)
+    tab = x.block_table.numpy()
+    slots = np.array([int(tab[b, p // 64]) * 64 + p % 64 for b in range(n_seq) for p in positions[b]])
+    got = case.pool[torch.from_numpy(slots).cuda()].double().cpu().numpy()
+    err = np.abs(got - exact) / _bf16_ulp(exact)
+    assert err.max() <= 1.0, f"a stored value is more than one bf16 step from the exact row ({err.max():.3f})"
+    record(f"cache_write ragged K, {n_seq * s_new} rows (max error in bf16 steps {err.max():.3f})",
+           *assert_close(got, exact, BF16_TOL, "rows"), n=got.size)
+
+
 # ------------------------------------------------------------------ query prologue
 
 def test_query_prologue_tiny_layer_f32():
@@ -252,6 +283,32 @@ def test_query_prologue_v3_slice():
     # oracle: the decode with the exact (float64) queries
     x.q_nope, x.q_pe = torch.from_numpy(want_n), torch.from_numpy(want_p)
     compare_sampled(case, out, lse, range(B), BF16_TOL, lse_tol=5e-3, what="query_prologue v3 -> decode")
+
+
+def test_query_prologue_ragged_k():
+    """d_model 7200 and d_h 96 (multiples of 32, not of 64): the W^Q / W^QR products (bf16 rows of
+    h) and the (W^UK_i)^T product (float32 q^C_i, K = d_h) both end their K chunks inside a block
+    of four k-steps.  16 heads, 20 sequences x 2 query tokens (two 32-row tiles of A)."""
+    _case("query_prologue ragged K")
+    from mla_latent_kv_03_amd import binding
+    n_h, B, s_q, d_model, d_h = 16, 20, 2, 7200, 96
+    w = workloads.layer_weights(1351, d_model=d_model, n_h=n_h, d_c=512, d_h=d_h, d_r=64, d_v=128,
+                                n_tokens=B * s_q, with_o=False)
+    lens = np.random.default_rng(1352).integers(10, 5000, size=B)
+    positions = np.array([[L - 2, L - 1] for L in lens], np.int32)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16)
+    h = bf(w["h"]).reshape(B, s_q, d_model)
+    wq, wqr = bf(w["q"]), bf(w["qr"])
+    uk_t = bf(np.transpose(w["uk"], (0, 2, 1)))
+    x = workloads.make_decode(lens.tolist(), s_q=s_q, n_h=n_h, page_size=64, seed=1353, d_c=512, d_r=64, d_v=128)
+    case = DeviceCase(x)
+    qn, qp = binding.mla_query_prologue(case.params, h.cuda(), wq.cuda(), uk_t.cuda(), wqr.cuda(),
+                                        torch.from_numpy(positions).cuda(), d_h=d_h)
+    torch.cuda.synchronize()
+    want_n, want_p = ref.query_rows(h.double().numpy(), wq.double().numpy(), bf(w["uk"]).double().numpy(),
+                                    wqr.double().numpy(), positions)
+    record("query_prologue ragged K q_nope", *assert_close(to_np(qn), want_n, BF16_TOL, "q_nope"), n=want_n.size)
+    record("query_prologue ragged K q_pe", *assert_close(to_np(qp), want_p, BF16_TOL, "q_pe"), n=want_p.size)
 
 
 # ------------------------------------------------------------------ output projection and fold
