@@ -6,7 +6,7 @@ import torch
 from mla_latent_kv_03_amd import workloads
 from oracle import mla_ref as ref
 
-from gpu_helpers import BF16_TOL, F32_TOL, DeviceCase, assert_close, to_np
+from gpu_helpers import BF16_TOL, F32_TOL, DeviceCase, assert_close, record, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -117,6 +117,59 @@ def test_standalone_combine_on_oracle_partials(kv):
     torch.cuda.synchronize()
     tol = BF16_TOL if kv == "bf16" else F32_TOL
     assert_close(to_np(out), o_ref, tol, "combine out")
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(fin, np.isfinite(to_np(lse)))
+    assert np.max(np.abs(to_np(lse)[fin] - lse_ref[fin])) <= 1e-5
+
+
+def test_standalone_combine_slot_counts():
+    """40 rows of 128 heads (two 32-row blocks, eight units per wave): slot counts that take every
+    merge path of the combine, oracle-made partials.  Units of at most 8 slots are merged all at
+    once per wave (at most 4 of them from the first loads, 5..8 with a second batch); a wave with a
+    unit of 9..64 slots takes the per-unit merge, and one of more than 64 its second loop."""
+    _print_case("combine slot counts")
+    rng = np.random.default_rng(204)
+    counts = [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 33, 64, 65, 70]
+    B = 40
+    parts = [counts[b] if b < len(counts) else int(rng.integers(1, 9)) for b in range(B)]
+    lens = [int(rng.integers(40, 300)) for _ in range(B)]
+    x = workloads.make_decode(lens, s_q=1, page_size=64, seed=205, n_h=128, d_c=512, d_r=64, d_v=128)
+    G = sum(parts)
+    case = DeviceCase(x, num_splits=G)
+    ws = case.binding.alloc_workspace(case.params)
+    table, plse, pu = case.binding.workspace_views(case.params, ws)
+    plse.fill_(float("nan"))
+    pu.fill_(float("nan"))
+    qn, qp = x.q_nope.double().numpy(), x.q_pe.double().numpy()
+    w = x.w_uv.double().numpy()
+    tab = np.zeros((B, 2), np.int32)
+    next_slot = 0
+    o_ref = np.zeros((B, 1, x.n_h, x.d_v))
+    lse_ref = np.full((B, 1, x.n_h), -np.inf)
+    for b in range(B):
+        L, n_parts = lens[b], parts[b]
+        c, kp = case.rows_of(b)
+        edges = [0, *sorted(rng.integers(0, L + 1, size=n_parts - 1)), L]
+        tab[b] = (next_slot, n_parts)
+        us, ls = [], []
+        for i in range(n_parts):
+            u_s, l_s = ref.split_partial(qn[b, 0], qp[b, 0], c, kp, x.softmax_scale, edges[i], edges[i + 1])
+            plse[next_slot + i, 0] = torch.from_numpy(l_s.astype(np.float32))
+            pu[next_slot + i, 0] = torch.from_numpy(u_s.astype(np.float32))
+            us.append(u_s)
+            ls.append(l_s)
+        u, l = ref.combine(np.array(us), np.array(ls))
+        o_ref[b, 0] = ref.up_project(u, w)
+        lse_ref[b, 0] = l
+        next_slot += n_parts
+    assert next_slot <= G + B
+    table.copy_(torch.from_numpy(tab))
+    out = torch.empty(B, 1, x.n_h, x.d_v, dtype=x.q_nope.dtype, device="cuda")
+    lse = torch.empty(B, 1, x.n_h, dtype=torch.float32, device="cuda")
+    case.binding.mla_decode_splitkv_combine(case.params, ws, case.w_uv, out, lse)
+    torch.cuda.synchronize()
+    record("standalone combine, 1..70 slots per row", *assert_close(to_np(out), o_ref, BF16_TOL, "combine out"),
+           n=o_ref.size)
     fin = np.isfinite(lse_ref)
     assert np.array_equal(fin, np.isfinite(to_np(lse)))
     assert np.max(np.abs(to_np(lse)[fin] - lse_ref[fin])) <= 1e-5
