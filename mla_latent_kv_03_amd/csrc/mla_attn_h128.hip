@@ -615,17 +615,17 @@ void attn_partial_h128(const AttnParams p) {
         // V^T fragment of this wave's column block cl (32 columns) and token half th of
         // tile it-1.
         auto vfrag = [&](int cl, int th) -> bf16x8 {
-          if constexpr (!FP8) {
-            const uint32_t o = 16384 * th;
-            const bf16x4 lo = lds_read_tr16(lds + ((bt ^ (64u * cl)) + o));
-            const bf16x4 hi = lds_read_tr16(lds + ((bt ^ (64u * cl ^ 32u)) + o + 8192));
-            return concat4(lo, hi);
-          } else {
-            const uint32_t o = 16 * LT::kVRow * th;
-            const u32x2 w8 = lds_read_tr8(lds + ((bt ^ (32u * cl)) + o));
-            return e4m3x8_to_bf16(w8[0], w8[1]);
-          }
+          const uint32_t o = 16384 * th;
+          const bf16x4 lo = lds_read_tr16(lds + ((bt ^ (64u * cl)) + o));
+          const bf16x4 hi = lds_read_tr16(lds + ((bt ^ (64u * cl ^ 32u)) + o + 8192));
+          return concat4(lo, hi);
         };
+        // E4M3: the 8-bit read and its widening are separate steps, a few k-steps apart, so
+        // that the widening does not wait for the read right after issuing it.
+        auto vraw8 = [&](int cl, int th) -> u32x2 {
+          return lds_read_tr8(lds + ((bt ^ (32u * cl)) + 16 * LT::kVRow * th));
+        };
+        auto widen = [&](u32x2 w8) -> bf16x8 { return e4m3x8_to_bf16(w8[0], w8[1]); };
         // P^T fragment of head block hb and token half th of tile it-1.
         auto pfrag = [&](int hb, int th) -> bf16x8 { return *(const bf16x8*)(lds + bp + (hb * 2 + th) * 1024); };
 
@@ -636,15 +636,21 @@ void attn_partial_h128(const AttnParams p) {
         // one wave per SIMD the reads' latency has to hide behind this wave's own MFMAs.
         f32x16 s;
         bf16x8 kq[kKPf + 1], va[4], pb[2][4];
-        u32x4 kr[2];          // E4M3: raw score operands, one k-step pair ahead
-        bf16x8 kop[2];        // E4M3: the current pair, widened exactly
+        u32x4 kr[2];          // E4M3: raw score operands, pair p in kr[p % 2], read two steps ahead
+        bf16x8 kop[2];        // E4M3: halves of the next pair, widened exactly one pair ahead of use
+        u32x2 vr[4];          // E4M3: value reads not yet widened
+        f32x4 tsc[4];         // E4M3: per-token scales of tile `it` (read before the score chain ends)
         if constexpr (!FP8) {
 #pragma unroll
           for (int j = 0; j < kKPf; ++j) kq[j] = kfrag(j);
+          va[0] = vfrag(0, 0);
         } else {
           kr[0] = kraw(0);
+          kr[1] = kraw(1);
+          vr[0] = vraw8(0, 0);                       // widened at ks = 1, first used at ks = 3
+          kop[0] = e4m3x8_to_bf16(kr[0][0], kr[0][1]);
+          kop[1] = e4m3x8_to_bf16(kr[0][2], kr[0][3]);
         }
-        va[0] = vfrag(0, 0);
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) pb[0][hb] = pfrag(hb, 0);
         // The copy bookkeeping of tile it+2 (scalar work) runs while those first reads are
@@ -659,22 +665,41 @@ void attn_partial_h128(const AttnParams p) {
           __builtin_amdgcn_sched_barrier(0);   // keep the source order: reads ahead of use
           if constexpr (!FP8) {
             if (ks + kKPf < kQk) kq[(ks + kKPf) % (kKPf + 1)] = kfrag(ks + kKPf);
-          } else if (ks % 2 == 0) {
-            if (ks / 2 + 1 < kQk / 2) kr[(ks / 2 + 1) % 2] = kraw(ks / 2 + 1);
-            const u32x4 r = kr[(ks / 2) % 2];
-            kop[0] = e4m3x8_to_bf16(r[0], r[1]);
-            kop[1] = e4m3x8_to_bf16(r[2], r[3]);
           }
           // Step a runs at ks = 2a + 3.  va[cl] holds token half 0 of column block cl
           // until its last use at ks = 8 cl + 9, then token half 1 (loaded 3 steps later).
-          if (ks == 2) va[1] = vfrag(1, 0);
-          if (ks == 10) va[2] = vfrag(2, 0);
-          if (ks == 18) va[3] = vfrag(3, 0);
-          if (ks == 12) va[0] = vfrag(0, 1);
-          if (ks == 20) va[1] = vfrag(1, 1);
-          if (ks == 28) va[2] = vfrag(2, 1);
+          if constexpr (!FP8) {
+            if (ks == 2) va[1] = vfrag(1, 0);
+            if (ks == 10) va[2] = vfrag(2, 0);
+            if (ks == 18) va[3] = vfrag(3, 0);
+            if (ks == 12) va[0] = vfrag(0, 1);
+            if (ks == 20) va[1] = vfrag(1, 1);
+            if (ks == 28) va[2] = vfrag(2, 1);
+            if (ks == 35) va[3] = vfrag(3, 1);
+          } else {
+            // The same loads, each widened two k-steps after its read (half 1 of column
+            // block 3 at the start of phase 2).
+            if (ks == 1) va[0] = widen(vr[0]);
+            if (ks == 2) vr[1] = vraw8(1, 0);
+            if (ks == 4) va[1] = widen(vr[1]);
+            if (ks == 10) vr[2] = vraw8(2, 0);
+            if (ks == 12) va[2] = widen(vr[2]);
+            if (ks == 18) vr[3] = vraw8(3, 0);
+            if (ks == 20) va[3] = widen(vr[3]);
+            if (ks == 12) vr[0] = vraw8(0, 1);
+            if (ks == 14) va[0] = widen(vr[0]);
+            if (ks == 20) vr[1] = vraw8(1, 1);
+            if (ks == 22) va[1] = widen(vr[1]);
+            if (ks == 28) vr[2] = vraw8(2, 1);
+            if (ks == 30) va[2] = widen(vr[2]);
+            if (ks == 35) vr[3] = vraw8(3, 1);
+            if (ks == 33) {
+              const uint32_t so = (uint32_t)offsetof(Smem<FP8>, sc) + ks3 * 256 + 16 * (lane_id_opaque() >> 5);
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4) tsc[g4] = *(const f32x4*)((const unsigned char*)&sm + so + 32 * g4);
+            }
+          }
           if (ks >= 30 && ks < 34) pb[1][ks - 30] = pfrag(ks - 30, 1);
-          if (ks == 35) va[3] = vfrag(3, 1);
           if (!FP8 && ks % 4 == 1) copy_row(tn, ks / 4, lo.ln);                     // ks = 1, 5, .., 33
           if (FP8 && ks % 8 == 1) copy_row(tn, ks / 8, lo.ln);                      // ks = 1, 9, .., 33
           const bf16x8 ka = FP8 ? kop[ks % 2] : kq[ks % (kKPf + 1)];
@@ -682,6 +707,17 @@ void attn_partial_h128(const AttnParams p) {
             score_mfma_first(s, ka, qf[ks]);
           else
             score_mfma(s, ka, qf[ks]);
+          if constexpr (FP8) {
+            // After step ks's MFMA (pair p = ks / 2): the same half of pair p + 1, read two
+            // steps ago, is widened into the register step ks used; at the pair's first step
+            // pair p + 2 is read into the slot that pair p has left.
+            const int pn = ks / 2 + 1;
+            if (pn < kQk / 2) {
+              const u32x4 r = kr[pn % 2];
+              kop[ks % 2] = ks % 2 == 0 ? e4m3x8_to_bf16(r[0], r[1]) : e4m3x8_to_bf16(r[2], r[3]);
+            }
+            if (ks % 2 == 0 && pn + 1 < kQk / 2) kr[(pn + 1) % 2] = kraw(pn + 1);
+          }
           if (ks >= 3 && ks % 2 == 1 && ks < 35) {
             const int a = (ks - 3) / 2;
             acc[a] = mfma32(va[a / 4], pb[0][a % 4], acc[a]);
@@ -696,11 +732,7 @@ void attn_partial_h128(const AttnParams p) {
         // E4M3: the per-token scales of tile `it` for this lane's tokens 8 g + 4h + i; the
         // key rows were widened without them, so they multiply the scores here and the
         // probabilities below (value rows).
-        f32x4 tsc[4];
         if constexpr (FP8) {
-          const uint32_t so = (uint32_t)offsetof(Smem<FP8>, sc) + ks3 * 256 + 16 * (lane_id_opaque() >> 5);
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) tsc[g4] = *(const f32x4*)((const unsigned char*)&sm + so + 32 * g4);
 #pragma unroll
           for (int v = 0; v < 16; ++v) s[v] *= tsc[v >> 2][v & 3];
         }
@@ -762,6 +794,7 @@ void attn_partial_h128(const AttnParams p) {
         for (int g = 0; g < 16; ++g) {
           __builtin_amdgcn_sched_barrier(0);
           acc[g] = mfma32(va[g / 4], pb[1][g % 4], acc[g]);
+          if (FP8 && g == 1) va[3] = widen(vr[3]);   // first use at g = 12
           if (g < 4) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
