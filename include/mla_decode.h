@@ -233,8 +233,9 @@ mla_status_t mla_set_attention_events(void* start, void* stop);
  * row-major; every product contracts over the last (contiguous) index of both operands.
  * bf16 operands (params->q_dtype / w_dtype == BF16) run on MFMAs with float32
  * accumulation and need the contraction width a multiple of 32, the other product
- * widths multiples of 16 and 16-byte aligned operand pointers; float32 operands accept
- * any size.  RoPE rotates interleaved pairs (x[2m], x[2m+1]) at position p by the angle
+ * widths multiples of 16 and 16-byte aligned operand pointers, and each activation
+ * operand (h, q^C, o or u) below 2 GiB (a weight of 2 GiB or more runs as several launches
+ * over its rows); float32 operands accept any size.  RoPE rotates interleaved pairs (x[2m], x[2m+1]) at position p by the angle
  * p * rope_base^(-2m/d_r), taken in float64.  Each call needs a workspace of the size
  * its *_workspace_size function returns (0 means invalid params); a workspace too small
  * gives MLA_ERR_WORKSPACE.  None of them reads seq_lens.

@@ -17,11 +17,13 @@ size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 mla_status_t status_of(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+// The bf16 product kernel addresses an activation operand through 32-bit offsets.
+bool act_fits(long long rows, long long width, int elem_bytes) { return rows * width * elem_bytes < (1LL << 31); }
 
 // K split of C[M, N] = A[M, K] B[N, K]^T.  bf16 weights: about four waves of the
 // weight-streaming kernel per compute unit (1024 waves, each a block of 32 or 64 rows of B
-// times a row tile of A), with chunks of at least 256 (a multiple of 16); float32 operands
-// use one chunk.
+// times a row tile of A), with chunks of at least 256 (multiples of 64 where K is, else of
+// 16); float32 operands use one chunk.
 struct Split {
   int ksplit, kchunk;
 };
@@ -82,6 +84,7 @@ mla_status_t check_cache_write(const mla_decode_params_t* p, int32_t d_model, in
   if (p->kv_dtype == MLA_DTYPE_F32 && bf16) return MLA_ERR_DTYPE;
   if (bf16 && (d_model % 32 || p->d_c % 16 || p->d_r % 16)) return MLA_ERR_SHAPE;
   const long long T = (long long)p->batch * s_new;
+  if (bf16 && !act_fits(T, d_model, 2)) return MLA_ERR_SHAPE;
   l.sp = split_of(T, p->d_c + p->d_r, d_model, bf16);
   l.rows = a256((size_t)l.sp.ksplit * T * (p->d_c + p->d_r) * sizeof(float));
   l.bytes = l.rows + a256((size_t)T * (p->d_c + p->d_r) * sizeof(float));
@@ -107,6 +110,7 @@ mla_status_t check_query(const mla_decode_params_t* p, int32_t d_model, int32_t 
   if (bf16 && (d_model % 32 || d_h % 32 || p->d_c % 16 || (p->n_h * p->d_r) % 16 || (p->n_h * d_h) % 16))
     return MLA_ERR_SHAPE;
   const long long T = (long long)p->batch * p->s_q;
+  if (bf16 && (!act_fits(T, d_model, 2) || !act_fits(T * p->n_h, d_h, 4))) return MLA_ERR_SHAPE;
   l.sc = split_of(T, (long long)p->n_h * d_h, d_model, bf16);
   l.sr = split_of(T, (long long)p->n_h * p->d_r, d_model, bf16);
   l.part_c = 0;
@@ -128,6 +132,7 @@ mla_status_t check_output(const mla_decode_params_t* p, int32_t d_model, int32_t
   if (!bf16 && x_dtype != MLA_DTYPE_F32) return MLA_ERR_DTYPE;
   if (bf16 && (width % 32 || d_model % 16)) return MLA_ERR_SHAPE;
   const long long M = (long long)p->batch * p->s_q;
+  if (bf16 && !act_fits(M, width, x_dtype == MLA_DTYPE_F32 ? 4 : 2)) return MLA_ERR_SHAPE;
   sp = split_of(M, d_model, width, bf16, x_dtype == MLA_DTYPE_F32);
   bytes = a256((size_t)sp.ksplit * M * d_model * sizeof(float));
   return MLA_OK;
