@@ -46,8 +46,11 @@ __device__ __forceinline__ int u_pos(int i, int k) { return i * kDc + ((((k >> 3
 //  remainder (about 16 significant bits).
 //  Phase 2: O[RB x 128] = U W^UV_i^T on 16x16x32 MFMAs; wave w owns output columns
 //  16 w .. 16 w + 15.
-template <int RB>
-__global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const CombineParams p) {
+//  EARLY_W: the W^UV rows are loaded first, with everything else (one workgroup per CU);
+//  otherwise after the merge, so that the merge's registers and W^UV's are not live together
+//  and two workgroups fit on a CU (grids of more than one workgroup per CU).
+template <int RB, bool EARLY_W>
+__device__ __forceinline__ void combine_upproj_body(const CombineParams& p) {
   constexpr int kUnits = 2 * RB;
   constexpr int P = kUnits >= kCombineWaves ? 1 : kCombineWaves / kUnits;   // waves per unit
   constexpr int M = kUnits >= kCombineWaves ? kUnits / kCombineWaves : 1;   // units per wave
@@ -68,11 +71,12 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const 
   const size_t slot_bytes = step * kDc * sizeof(bf16);
 
   bf16x8 bw[kDc / 32];
-  if (p.w_uv) {
+  auto load_w = [&]() {
     const bf16* wrow = (const bf16*)p.w_uv + ((size_t)head * kDv + 16 * wave + l16) * kDc + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < kDc / 32; ++kk) bw[kk] = *(const bf16x8*)(wrow + kk * 32);
-  }
+  };
+  if (EARLY_W && p.w_uv) load_w();
 
   // Units of this wave: m-th unit u = wave / P (P > 1) or wave + 8 m; row u / 2, half u % 2.
   // The split-table entries are loaded unconditionally (rows past the block clamp to the
@@ -256,6 +260,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const 
 #pragma unroll
     for (int m = 0; m < M; ++m) store_u(u_row[m], u_half[m], all_fit ? accumulate(m) : finish(m));
   }
+  if (!EARLY_W && p.w_uv) load_w();
   __syncthreads();
   if (!p.w_uv) return;   // kernel-uniform
 
@@ -279,6 +284,16 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const 
       if (ri < nrows) out[((size_t)(row0 + ri) * p.n_h + head) * kDv + 16 * wave + l16] = (bf16)o[i];
     }
   }
+}
+
+template <int RB>
+__global__ __launch_bounds__(64 * kCombineWaves) void combine_upproj_bf16(const CombineParams p) {
+  combine_upproj_body<RB, true>(p);
+}
+template <int RB>
+__global__ __launch_bounds__(64 * kCombineWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void combine_upproj_bf16_2pc(const CombineParams p) {
+  combine_upproj_body<RB, false>(p);
 }
 
 // float32 path: one workgroup per (head, 16 rows), any d_c <= 1024 and d_v.
@@ -342,6 +357,11 @@ hipError_t launch_combine_bf16(const CombineParams& p, hipStream_t stream) {
   while (rb > 1 && (long long)p.n_h * ((R + rb - 1) / rb) < 256) rb /= 2;
   dim3 grid(p.n_h, (R + rb - 1) / rb);
   dim3 block(64 * kCombineWaves);
+  if (rb == 32 && (long long)grid.x * grid.y > 256) {
+    // More workgroups than CUs: the variant that fits two per CU.
+    hipLaunchKernelGGL(combine_upproj_bf16_2pc<32>, grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
   switch (rb) {
     case 32: hipLaunchKernelGGL(combine_upproj_bf16<32>, grid, block, 0, stream, p); break;
     case 16: hipLaunchKernelGGL(combine_upproj_bf16<16>, grid, block, 0, stream, p); break;
