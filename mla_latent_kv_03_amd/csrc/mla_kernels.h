@@ -70,10 +70,12 @@ struct AppendParams {
 struct GemmArgs {
   const void* a;
   const void* b;
+  const void* b2;            // bf16 product: rows n >= n_split of B are row n - n_split of b2 (or null)
   void* c;                   // float32 partials, or bf16 when out_bf16 (one chunk only)
   int64_t lda, ldb, ldc;
   int64_t a_bs, b_bs, c_bs, c_ks;
   int32_t M, N, K, kchunk, batch;
+  int32_t n_split;           // with b2: a multiple of the rows of B one wave covers (32, float32 A 64)
   int32_t a_f32;             // bf16 operands: A is float32 (enters as bf16 high + remainder)
   int32_t out_bf16;
 };
@@ -81,7 +83,9 @@ struct GemmArgs {
 // Cache write finish: sums the partials [ksplit][T][d_c + d_r] of each new token's row,
 // rotates its RoPE part and writes the pool slot.
 struct CacheWriteArgs {
-  const float* part;         // summed rows [T][d_c + d_r]
+  const float* part;         // partial j of row t at part + j * part_ks + t * (d_c + d_r)
+  int64_t part_ks;
+  int32_t ksplit;
   int32_t d_c, d_r, s_new;
   const int32_t* positions;
   const int32_t* block_table;

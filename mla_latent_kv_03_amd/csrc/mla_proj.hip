@@ -95,14 +95,19 @@ __global__ __launch_bounds__(64 * kGemmWaves) void gemm_stream(const GemmArgs g)
   if (nsteps <= 0) return;                           // workgroup-uniform
   const int nblocks = (nsteps + 3) >> 2;
 
-  // B copy i of a block: rows 8 i .. 8 i + 7 of the wave's 32 NB rows.
-  const int64_t b_bytes = ((int64_t)(g.N - 1) * g.ldb + g.K) * 2;
-  const __amdgpu_buffer_rsrc_t rs_b = buffer_rsrc((const bf16*)g.b + bt * g.b_bs, (int)min(b_bytes, (int64_t)INT32_MAX));
+  // B copy i of a block: rows 8 i .. 8 i + 7 of the wave's 32 NB rows, from b or, past
+  // n_split, from b2 (a wave's rows lie in one of them).
+  const bool second = g.b2 != nullptr && n0 >= g.n_split;
+  const int b_rows = g.b2 == nullptr ? g.N : second ? g.N - g.n_split : g.n_split;
+  const int nb0 = second ? n0 - g.n_split : n0;
+  const int64_t b_bytes = ((int64_t)(b_rows - 1) * g.ldb + g.K) * 2;
+  const __amdgpu_buffer_rsrc_t rs_b =
+      buffer_rsrc((const bf16*)(second ? g.b2 : g.b) + bt * g.b_bs, (int)min(b_bytes, (int64_t)INT32_MAX));
   uint32_t vo_b[kBCopies];
 #pragma unroll
   for (int i = 0; i < kBCopies; ++i) {
     const int r = 8 * i + (lane >> 3);
-    vo_b[i] = (uint32_t)((int64_t)min(n0 + r, g.N - 1) * g.ldb * 2) + 16u * (uint32_t)((lane & 7) ^ (r & 7));
+    vo_b[i] = (uint32_t)((int64_t)min(nb0 + r, b_rows - 1) * g.ldb * 2) + 16u * (uint32_t)((lane & 7) ^ (r & 7));
   }
   unsigned char* const bring = lds + SA * kASlot + wave * RA * kBBlock;
   auto copy_b = [&](int blk) {
@@ -277,73 +282,87 @@ __device__ __forceinline__ float rope_lane(float v, int pair, int d_r, int pos, 
   return odd ? __builtin_fmaf(partner, sn, v * cs) : __builtin_fmaf(-partner, sn, v * cs);
 }
 
-constexpr int kMaxRowPerLane = 20;   // d_c + d_r <= 1280
-
-// One wave per new token: reads its summed [c | k^R_raw] row (float32; the K-split
-// partials are added by sum_partials first), rotates the RoPE part at the token's position
-// and writes the pool slot (same slot rule and skips as the append kernel; same E4M3
-// quantizer).
-__global__ __launch_bounds__(64) void cache_write_finish(const CacheWriteArgs a) {
+// One workgroup per new token, one thread per pair of row elements (the pair a RoPE
+// rotation mixes; d_c is even): sums the pair's K-split partials in chunk order, rotates it
+// if it lies in the RoPE part, and writes the pool slot (same slot rule and skips as the
+// append kernel; same E4M3 quantizer on the float32 row, its amax reduced over the
+// workgroup).  d_c + d_r <= 1280, so at most 640 threads.
+__global__ __launch_bounds__(640) void cache_write_finish(const CacheWriteArgs a) {
+  __shared__ float wave_amax[10];
   const int tok = blockIdx.x;
   const int b = tok / a.s_new;
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x;
   const int pos = a.positions[tok];
-  if (pos < 0) return;
+  if (pos < 0) return;                                       // workgroup-uniform skips
   const int page_idx = pos / a.page_size;
   if (page_idx >= a.max_pages) return;
   const int page = a.block_table[(size_t)b * a.max_pages + page_idx];
   if (page < 0 || page >= a.num_pages) return;
   const long long slot = (long long)page * a.page_size + pos % a.page_size;
   const int D = a.d_c + a.d_r;
-  float v[kMaxRowPerLane];
+  const int e = 2 * t;
+  const bool in = e < D;
+  float x = 0.f, y = 0.f;
+  if (in) {
+    // 16 partials in flight at a time (chunks past ksplit read chunk 0 and are not added).
+    const float* src = a.part + (int64_t)tok * D + e;
+    for (int j0 = 0; j0 < a.ksplit; j0 += 16) {
+      f32x2 p[16];
 #pragma unroll
-  for (int j = 0; j < kMaxRowPerLane; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = e < D ? a.part[(int64_t)tok * D + e] : 0.f;
-  }
+      for (int i = 0; i < 16; ++i) {
+        const int j = j0 + i < a.ksplit ? j0 + i : 0;
+        p[i] = *(const f32x2*)(src + (int64_t)j * a.part_ks);
+      }
 #pragma unroll
-  for (int j = 0; j < kMaxRowPerLane; ++j) {
-    const int e = lane + 64 * j;
-    if (64 * j + 63 < a.d_c || 64 * j >= D) continue;        // wave-uniform: no RoPE element in this group
-    const bool rot = e >= a.d_c && e < D;
-    const float r = rope_lane(v[j], (e - a.d_c) >> 1, a.d_r, pos, a.rope_base, (lane & 1) != 0);
-    if (rot) v[j] = r;
+      for (int i = 0; i < 16; ++i)
+        if (j0 + i < a.ksplit) {
+          x += p[i][0];
+          y += p[i][1];
+        }
+    }
+    if (e >= a.d_c) {
+      const double theta = pow((double)a.rope_base, -2.0 * (double)((e - a.d_c) >> 1) / (double)a.d_r);
+      double sd, cd;
+      sincos((double)pos * theta, &sd, &cd);
+      const float cs = (float)cd, sn = (float)sd;
+      const float xr = __builtin_fmaf(-y, sn, x * cs), yr = __builtin_fmaf(x, sn, y * cs);
+      x = xr;
+      y = yr;
+    }
   }
   if (a.mode == 0 || a.mode == 1) {
-#pragma unroll
-    for (int j = 0; j < kMaxRowPerLane; ++j) {
-      const int e = lane + 64 * j;
-      if (e >= D) continue;
-      if (a.mode == 0) {
-        if (e < a.d_c) ((bf16*)a.c_kv)[slot * a.c_stride + e] = (bf16)v[j];
-        else ((bf16*)a.k_pe)[slot * a.k_stride + e - a.d_c] = (bf16)v[j];
-      } else {
-        if (e < a.d_c) ((float*)a.c_kv)[slot * a.c_stride + e] = v[j];
-        else ((float*)a.k_pe)[slot * a.k_stride + e - a.d_c] = v[j];
-      }
+    if (!in) return;
+    const bool kpart = e >= a.d_c;
+    const long long o = kpart ? slot * a.k_stride + e - a.d_c : slot * a.c_stride + e;
+    if (a.mode == 0) {
+      bf16* dst = (bf16*)(kpart ? a.k_pe : a.c_kv) + o;
+      dst[0] = (bf16)x;
+      dst[1] = (bf16)y;
+    } else {
+      float* dst = (float*)(kpart ? a.k_pe : a.c_kv) + o;
+      dst[0] = x;
+      dst[1] = y;
     }
     return;
   }
-  // E4M3 + per-token scale (the append kernel's quantizer on the float32 row).
-  float amax = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxRowPerLane; ++j)
-    if (lane + 64 * j < D) amax = fmaxf(amax, fabsf(v[j]));
-  amax = wave_max(amax);
+  // E4M3 + per-token scale.
+  float amax = wave_max(fmaxf(fabsf(x), fabsf(y)));
+  if ((t & 63) == 0) wave_amax[t >> 6] = amax;
+  __syncthreads();
+  amax = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) amax = fmaxf(amax, wave_amax[w]);
   float inv = 1.f, scale = 1.f;
   if (amax > 0.f) {
     inv = __fdiv_rn(448.f, amax);
     scale = __fdiv_rn(amax, 448.f);
   }
-#pragma unroll
-  for (int j = 0; j < kMaxRowPerLane; ++j) {
-    const int e = lane + 64 * j;
-    if (e >= D) continue;
-    const uint8_t code = (uint8_t)f32_to_e4m3(__fmul_rn(v[j], inv));
-    if (e < a.d_c) ((uint8_t*)a.c_kv)[slot * a.c_stride + e] = code;
-    else ((uint8_t*)a.k_pe)[slot * a.k_stride + e - a.d_c] = code;
+  if (in) {
+    const bool kpart = e >= a.d_c;
+    uint8_t* dst = (uint8_t*)(kpart ? a.k_pe : a.c_kv) + (kpart ? slot * a.k_stride + e - a.d_c : slot * a.c_stride + e);
+    dst[0] = (uint8_t)f32_to_e4m3(__fmul_rn(x, inv));
+    dst[1] = (uint8_t)f32_to_e4m3(__fmul_rn(y, inv));
   }
-  if (lane == 0) a.kv_scale[slot] = scale;
+  if (t == 0) a.kv_scale[slot] = scale;
 }
 
 // Query prologue finish, one thread per element: the first ceil(T n_h d_h / 256)
@@ -408,6 +427,8 @@ hipError_t launch_gemm_nt(const GemmArgs& g, bool bf16_operands, int ksplit, hip
     const int64_t a_bytes = ((int64_t)(g.M - 1) * g.lda + g.K) * (g.a_f32 ? 4 : 2);
     if (a_bytes >= max_bytes) return hipErrorInvalidValue;
     const int64_t b_bytes = ((int64_t)(g.N - 1) * g.ldb + g.K) * 2;
+    if (g.b2 != nullptr && (b_bytes >= max_bytes || g.n_split % (32 * gemm_col_blocks(g.a_f32 != 0)) != 0))
+      return hipErrorInvalidValue;
     if (b_bytes >= max_bytes) {
       const int rows = (int)((max_bytes / 2 - g.K) / g.ldb) & ~127;   // whole workgroups of B rows
       if (rows < 128) return hipErrorInvalidValue;
@@ -448,7 +469,8 @@ hipError_t launch_gemm_nt(const GemmArgs& g, bool bf16_operands, int ksplit, hip
 }
 
 hipError_t launch_cache_write_finish(const CacheWriteArgs& a, int tokens, hipStream_t s) {
-  hipLaunchKernelGGL(cache_write_finish, dim3(tokens), dim3(64), 0, s, a);
+  const int waves = (a.d_c + a.d_r + 127) / 128;   // one thread per element pair
+  hipLaunchKernelGGL(cache_write_finish, dim3(tokens), dim3(64 * waves), 0, s, a);
   return hipGetLastError();
 }
 

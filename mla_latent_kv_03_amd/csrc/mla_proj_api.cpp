@@ -46,6 +46,7 @@ mla::GemmArgs gemm(const void* a, int64_t lda, const void* b, int64_t ldb, void*
   mla::GemmArgs g{};
   g.a = a;
   g.b = b;
+  g.b2 = nullptr;
   g.c = c;
   g.lda = lda;
   g.ldb = ldb;
@@ -57,6 +58,7 @@ mla::GemmArgs gemm(const void* a, int64_t lda, const void* b, int64_t ldb, void*
   g.K = K;
   g.kchunk = sp.kchunk;
   g.batch = 1;
+  g.n_split = N;
   g.a_f32 = 0;
   g.out_bf16 = 0;
   return g;
@@ -68,7 +70,7 @@ bool is_in_dtype(mla_dtype_t t) { return t == MLA_DTYPE_BF16 || t == MLA_DTYPE_F
 
 struct CacheWriteLayout {
   Split sp;
-  size_t rows, bytes;   // K-split partials [ksplit][T][d_c + d_r] at 0, summed rows at `rows`
+  size_t bytes;         // K-split partials [ksplit][T][d_c + d_r]
 };
 
 mla_status_t check_cache_write(const mla_decode_params_t* p, int32_t d_model, int32_t s_new, CacheWriteLayout& l) {
@@ -86,8 +88,7 @@ mla_status_t check_cache_write(const mla_decode_params_t* p, int32_t d_model, in
   const long long T = (long long)p->batch * s_new;
   if (bf16 && !act_fits(T, d_model, 2)) return MLA_ERR_SHAPE;
   l.sp = split_of(T, p->d_c + p->d_r, d_model, bf16);
-  l.rows = a256((size_t)l.sp.ksplit * T * (p->d_c + p->d_r) * sizeof(float));
-  l.bytes = l.rows + a256((size_t)T * (p->d_c + p->d_r) * sizeof(float));
+  l.bytes = a256((size_t)l.sp.ksplit * T * (p->d_c + p->d_r) * sizeof(float));
   return MLA_OK;
 }
 
@@ -171,19 +172,27 @@ mla_status_t mla_cache_write(const mla_decode_params_t* params, int32_t d_model,
   const int T = p.batch * s_new, D = p.d_c + p.d_r;
   float* part = (float*)workspace;
   const int64_t part_ks = (int64_t)T * D;
-  mla::GemmArgs g = gemm(h, d_model, w_dkv, d_model, part, D, T, p.d_c, d_model, l.sp, part_ks);
-  st = status_of(mla::launch_gemm_nt(g, bf16, l.sp.ksplit, s));
-  if (st != MLA_OK) return st;
-  if (p.d_r > 0) {
-    g = gemm(h, d_model, w_kr, d_model, part + p.d_c, D, T, p.d_r, d_model, l.sp, part_ks);
+  if (bf16 && p.d_r > 0 && p.d_c % 32 == 0) {
+    // One product over [W^DKV; W^KR]: the rows past d_c come from w_kr.
+    mla::GemmArgs g = gemm(h, d_model, w_dkv, d_model, part, D, T, D, d_model, l.sp, part_ks);
+    g.b2 = w_kr;
+    g.n_split = p.d_c;
     st = status_of(mla::launch_gemm_nt(g, bf16, l.sp.ksplit, s));
     if (st != MLA_OK) return st;
+  } else {
+    mla::GemmArgs g = gemm(h, d_model, w_dkv, d_model, part, D, T, p.d_c, d_model, l.sp, part_ks);
+    st = status_of(mla::launch_gemm_nt(g, bf16, l.sp.ksplit, s));
+    if (st != MLA_OK) return st;
+    if (p.d_r > 0) {
+      g = gemm(h, d_model, w_kr, d_model, part + p.d_c, D, T, p.d_r, d_model, l.sp, part_ks);
+      st = status_of(mla::launch_gemm_nt(g, bf16, l.sp.ksplit, s));
+      if (st != MLA_OK) return st;
+    }
   }
-  float* rows = (float*)((char*)workspace + l.rows);
-  st = status_of(mla::launch_sum_partials(part, part_ks, l.sp.ksplit, part_ks, rows, false, s));
-  if (st != MLA_OK) return st;
   mla::CacheWriteArgs a;
-  a.part = rows;
+  a.part = part;
+  a.part_ks = part_ks;
+  a.ksplit = l.sp.ksplit;
   a.d_c = p.d_c;
   a.d_r = p.d_r;
   a.s_new = s_new;
