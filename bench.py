@@ -18,6 +18,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -396,10 +397,11 @@ def adjacent(args, dev):
     g = torch.Generator(device="cpu").manual_seed(6)
     rnd = lambda *shape, std=1.0: (torch.randn(*shape, generator=g) * std).to(torch.bfloat16).to(dev)
 
-    def time_us(fn, reps=20):
+    def time_us(fn, reps=20, batches=7):
         """GPU time of one call: the call's launches are captured once in a HIP graph (on a
-        side stream) and the graph is replayed `reps` times between two events, so that the
-        host-side marshalling of each call is not counted."""
+        side stream); after replays for at least 200 ms (clocks settle), `batches` batches of
+        `reps` replays are each timed between two events and the median batch is reported,
+        so that neither the host-side marshalling of each call nor a cold start is counted."""
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -412,13 +414,21 @@ def adjacent(args, dev):
         torch.cuda.current_stream().wait_stream(side)
         graph.replay()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            graph.replay()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / reps
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:
+            for _ in range(reps):
+                graph.replay()
+            torch.cuda.synchronize()
+        times = []
+        for _ in range(batches):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                graph.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3 / reps)
+        return statistics.median(times)
 
     def line(row, what, us, nbytes):
         gbs = nbytes / (us * 1e-6) / 1e9
