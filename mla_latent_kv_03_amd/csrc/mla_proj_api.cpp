@@ -20,10 +20,10 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 // The bf16 product kernel addresses an activation operand through 32-bit offsets.
 bool act_fits(long long rows, long long width, int elem_bytes) { return rows * width * elem_bytes < (1LL << 31); }
 
-// K split of C[M, N] = A[M, K] B[N, K]^T.  bf16 weights: about four waves of the
+// K split of C[M, N] = A[M, K] B[N, K]^T.  bf16 weights: at most four waves of the
 // weight-streaming kernel per compute unit (1024 waves, each a block of 32 or 64 rows of B
-// times a row tile of A), with chunks of at least 256 (multiples of 64 where K is, else of
-// 16); float32 operands use one chunk.
+// times a row tile of A, one workgroup per CU), with chunks of at least 256 (multiples of
+// 64 where K is, else of 16); float32 operands use one chunk.
 struct Split {
   int ksplit, kchunk;
 };
@@ -31,7 +31,10 @@ Split split_of(long long M, long long N, int K, bool bf16, bool a_f32 = false) {
   if (!bf16) return {1, K};
   const int rows = 32 * mla::gemm_row_blocks(M > INT_MAX ? INT_MAX : (int)M);
   const long long waves = (long long)cdiv(N, 32 * mla::gemm_col_blocks(a_f32)) * cdiv(M, rows);
-  long long ks = (1024 + waves - 1) / waves;
+  // Rounded down: a grid of a few more workgroups than CUs puts two on some CUs, which
+  // then stream twice the weights (W^O at 64 rows: K split 5, 280 workgroups, 59.7 us;
+  // K split 4, 224 workgroups, 47.8 us).
+  long long ks = 1024 / waves;
   const long long max_ks = K / 256 > 0 ? K / 256 : 1;
   if (ks > max_ks) ks = max_ks;
   if (ks < 1) ks = 1;
