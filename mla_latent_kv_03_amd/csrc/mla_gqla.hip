@@ -201,32 +201,49 @@ __global__ __launch_bounds__(64) void gqa_decode_partial(const GqaParams p) {
 
 // Merge the splits of every (sequence, group) row: lse = ln sum_s e^{lse_s},
 // o = sum_s e^{lse_s - lse} o_s; written as [B, s_q, n_h, d_v] (bf16) and lse [B, s_q, n_h].
+// Log-sum-exp merge of the splits: one thread per (row, output column), 256 / d_v rows per
+// workgroup; the lse values and the partial outputs of 8 splits are loaded together (no
+// load waits for another), the maximum and the sum first, then the weighted sum.
 __global__ __launch_bounds__(256) void gqa_combine(const GqaParams p) {
+  constexpr int kB = 8;
   const int g = blockIdx.y, b = blockIdx.z;
   const int hpg = p.n_h / p.n_g;
   const int R = hpg * p.s_q;
-  const int row = blockIdx.x;
+  const int rpw = 256 / p.d_v;
+  const int row = blockIdx.x * rpw + (int)threadIdx.x / p.d_v;
+  const int col = (int)threadIdx.x % p.d_v;
   if (row >= R) return;
   const size_t base = (((size_t)b * p.n_g + g) * p.splits) * 32 + row;
   float mx = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.part_lse[base + (size_t)s * 32]);
-  float tot = 0.f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float l = p.part_lse[base + (size_t)s * 32];
-    if (l != -INFINITY) tot += __expf(l - mx);
+  for (int s0 = 0; s0 < p.splits; s0 += kB) {
+    float l[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) l[i] = s0 + i < p.splits ? p.part_lse[base + (size_t)(s0 + i) * 32] : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kB; ++i) mx = fmaxf(mx, l[i]);
   }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  float tot = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < p.splits; s0 += kB) {
+    float l[kB], o[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const bool in = s0 + i < p.splits;
+      const size_t r = base + (size_t)(in ? s0 + i : 0) * 32;
+      l[i] = in ? p.part_lse[r] : -INFINITY;
+      o[i] = p.part_o[r * p.d_v + col];
+    }
+#pragma unroll
+    for (int i = 0; i < kB; ++i)
+      if (l[i] != -INFINITY) {
+        const float w = __expf(l[i] - mx);
+        tot += w;
+        acc += w * o[i];
+      }
+  }
   const int q_pos = row / hpg, head = g * hpg + row % hpg;
   const size_t orow = ((size_t)b * p.s_q + q_pos) * p.n_h + head;
-  for (int col = threadIdx.x; col < p.d_v; col += 256) {
-    float acc = 0.f;
-    for (int s = 0; s < p.splits; ++s) {
-      const float l = p.part_lse[base + (size_t)s * 32];
-      if (l != -INFINITY) acc += __expf(l - mx) * inv * p.part_o[(base + (size_t)s * 32) * p.d_v + col];
-    }
-    ((bf16*)p.out)[orow * p.d_v + col] = (bf16)acc;
-  }
-  if (threadIdx.x == 0 && p.lse) p.lse[orow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
+  ((bf16*)p.out)[orow * p.d_v + col] = (bf16)(tot > 0.f ? acc / tot : 0.f);
+  if (col == 0 && p.lse) p.lse[orow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
 }
 
 }  // namespace
@@ -242,7 +259,7 @@ hipError_t launch_gqa_decode(const GqaParams& p, hipStream_t s) {
 #undef MLA_GQA
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 cgrid(32, p.n_g, p.batch);
+  dim3 cgrid((32 + 256 / p.d_v - 1) / (256 / p.d_v), p.n_g, p.batch);
   hipLaunchKernelGGL(gqa_combine, cgrid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
