@@ -270,16 +270,15 @@ __global__ __launch_bounds__(256) void gemm_nt_f32(const GemmArgs g) {
 // Rotation of one interleaved pair (x, y) = (v[2m], v[2m+1]) of a d_r-wide RoPE vector at
 // position pos by angle pos * base^(-2m / d_r).  The angle and its sine and cosine are taken
 // in float64 (pos * theta reaches ~1.3e5 radians, where a float32 angle would be off by
-// ~1e-2); the rotation itself is float32.  Lanes hold consecutive elements, so the partner
-// of lane l is lane l ^ 1 (d_c and the element index of lane l have the parity of l).
-__device__ __forceinline__ float rope_lane(float v, int pair, int d_r, int pos, float base, bool odd) {
-  const double theta = pow((double)base, -2.0 * (double)pair / (double)d_r);
-  double s, c;
-  sincos((double)pos * theta, &s, &c);
-  const float partner = __shfl_xor(v, 1, 64);
-  const float cs = (float)c, sn = (float)s;
-  // even element: x cos - y sin; odd element: x sin + y cos
-  return odd ? __builtin_fmaf(partner, sn, v * cs) : __builtin_fmaf(-partner, sn, v * cs);
+// ~1e-2); the rotation itself is float32.
+__device__ __forceinline__ void rope_pair(float& x, float& y, int m, int d_r, int pos, float base) {
+  const double theta = pow((double)base, -2.0 * (double)m / (double)d_r);
+  double sd, cd;
+  sincos((double)pos * theta, &sd, &cd);
+  const float cs = (float)cd, sn = (float)sd;
+  const float xr = __builtin_fmaf(-y, sn, x * cs), yr = __builtin_fmaf(x, sn, y * cs);
+  x = xr;
+  y = yr;
 }
 
 // One workgroup per new token, one thread per pair of row elements (the pair a RoPE
@@ -320,15 +319,7 @@ __global__ __launch_bounds__(640) void cache_write_finish(const CacheWriteArgs a
           y += p[i][1];
         }
     }
-    if (e >= a.d_c) {
-      const double theta = pow((double)a.rope_base, -2.0 * (double)((e - a.d_c) >> 1) / (double)a.d_r);
-      double sd, cd;
-      sincos((double)pos * theta, &sd, &cd);
-      const float cs = (float)cd, sn = (float)sd;
-      const float xr = __builtin_fmaf(-y, sn, x * cs), yr = __builtin_fmaf(x, sn, y * cs);
-      x = xr;
-      y = yr;
-    }
+    if (e >= a.d_c) rope_pair(x, y, (e - a.d_c) >> 1, a.d_r, pos, a.rope_base);
   }
   if (a.mode == 0 || a.mode == 1) {
     if (!in) return;
@@ -365,34 +356,63 @@ __global__ __launch_bounds__(640) void cache_write_finish(const CacheWriteArgs a
   if (t == 0) a.kv_scale[slot] = scale;
 }
 
-// Query prologue finish, one thread per element: the first ceil(T n_h d_h / 256)
-// workgroups sum the K-split partials of q^C into float32 scratch (the absorption
-// product's input), the others sum those of q^R_raw and rotate each interleaved pair by
-// its token's position (the partner element is in the neighbouring lane: n_h d_r is even,
-// so pairs never straddle a workgroup, a token or a head).
+// Query prologue finish, four consecutive elements per thread (16-byte loads and stores
+// when the widths allow; the partials of 8 K-chunks loaded together): the first
+// ceil(T n_h d_h / 1024) workgroups sum the K-split partials of q^C into float32 scratch
+// (the absorption product's input), the others sum those of q^R_raw and rotate each of
+// their two interleaved pairs by its token's position (n_h d_r and d_r are even, so a pair
+// never straddles a token or a head).
+__device__ __forceinline__ f32x4 sum_partials4(const float* src, int64_t ks_stride, int ksplit, int n) {
+  constexpr int kB = 8;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (n == 4 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 && (ks_stride & 3) == 0) {
+    for (int j0 = 0; j0 < ksplit; j0 += kB) {
+      f32x4 p[kB];
+#pragma unroll
+      for (int i = 0; i < kB; ++i) p[i] = *(const f32x4*)(src + (int64_t)(j0 + i < ksplit ? j0 + i : 0) * ks_stride);
+#pragma unroll
+      for (int i = 0; i < kB; ++i)
+        if (j0 + i < ksplit) v += p[i];
+    }
+    return v;
+  }
+  for (int k = 0; k < n; ++k)
+    for (int j = 0; j < ksplit; ++j) v[k] += src[(int64_t)j * ks_stride + k];
+  return v;
+}
+
 __global__ __launch_bounds__(256) void query_finish(const QueryArgs a, int tokens, int c_blocks) {
   const int64_t nc = (int64_t)tokens * a.n_h * a.d_h, nr = (int64_t)tokens * a.n_h * a.d_r;
   if ((int)blockIdx.x < c_blocks) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= nc) return;
-    float v = 0.f;
-    for (int ks = 0; ks < a.ksplit; ++ks) v += a.part_c[(int64_t)ks * a.part_c_ks + e];
-    a.q_c[e] = v;
+    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e0 >= nc) return;
+    const int n = (int)min((int64_t)4, nc - e0);
+    const f32x4 v = sum_partials4(a.part_c + e0, a.part_c_ks, a.ksplit, n);
+    if (n == 4 && (nc & 3) == 0) *(f32x4*)(a.q_c + e0) = v;
+    else
+      for (int k = 0; k < n; ++k) a.q_c[e0 + k] = v[k];
     return;
   }
-  const int64_t e = (int64_t)(blockIdx.x - c_blocks) * 256 + threadIdx.x;
-  const bool in = e < nr;
-  const int64_t ec = in ? e : nr - 1;
+  const int64_t e0 = ((int64_t)(blockIdx.x - c_blocks) * 256 + threadIdx.x) * 4;
+  if (e0 >= nr) return;
+  const int n = (int)min((int64_t)4, nr - e0);
+  f32x4 v = sum_partials4(a.part_r + e0, a.part_r_ks, a.ksplit_r, n);
   const int per_tok = a.n_h * a.d_r;
-  const int tok = (int)(ec / per_tok);
-  const int within = (int)(ec - (int64_t)tok * per_tok) % a.d_r;
-  float v = 0.f;
-  if (in)
-    for (int ks = 0; ks < a.ksplit_r; ++ks) v += a.part_r[(int64_t)ks * a.part_r_ks + e];
-  const float r = rope_lane(v, within >> 1, a.d_r, a.positions[tok], a.rope_base, (threadIdx.x & 1) != 0);
-  if (!in) return;
-  if (a.out_bf16) ((bf16*)a.q_pe)[e] = (bf16)r;
-  else ((float*)a.q_pe)[e] = r;
+#pragma unroll
+  for (int k = 0; k < 4; k += 2) {
+    if (k >= n) break;
+    const int64_t e = e0 + k;
+    const int tok = (int)(e / per_tok);
+    const int within = (int)(e - (int64_t)tok * per_tok) % a.d_r;
+    float x = v[k], y = v[k + 1];
+    rope_pair(x, y, within >> 1, a.d_r, a.positions[tok], a.rope_base);
+    v[k] = x;
+    v[k + 1] = y;
+  }
+  for (int k = 0; k < n; ++k) {
+    if (a.out_bf16) ((bf16*)a.q_pe)[e0 + k] = (bf16)v[k];
+    else ((float*)a.q_pe)[e0 + k] = v[k];
+  }
 }
 
 // Sum of K-split partials [ksplit][n] into out (float32 or bf16), n elements.
@@ -476,7 +496,7 @@ hipError_t launch_cache_write_finish(const CacheWriteArgs& a, int tokens, hipStr
 
 hipError_t launch_query_finish(const QueryArgs& a, int tokens, hipStream_t s) {
   const int64_t nc = (int64_t)tokens * a.n_h * a.d_h, nr = (int64_t)tokens * a.n_h * a.d_r;
-  const int c_blocks = (int)((nc + 255) / 256), r_blocks = (int)((nr + 255) / 256);
+  const int c_blocks = (int)((nc + 1023) / 1024), r_blocks = (int)((nr + 1023) / 1024);
   hipLaunchKernelGGL(query_finish, dim3(c_blocks + r_blocks), dim3(256), 0, s, a, tokens, c_blocks);
   return hipGetLastError();
 }
