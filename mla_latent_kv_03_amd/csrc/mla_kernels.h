@@ -109,6 +109,10 @@ struct QueryArgs {
   void* q_pe;                // [T][n_h * d_r]
   int32_t out_bf16;
   float rope_base;
+  // bf16 queries, query_absorb only: (W^UK_i)^T [n_h][d_c][d_h] and q~ out [T][n_h][d_c]
+  const void* w_uk_t;
+  void* q_nope;
+  int32_t d_c;
 };
 
 // GQLA per-group decode (mla_gqla.hip): split partials [B][n_g][splits][32 rows][d_v] and
@@ -139,6 +143,9 @@ inline int gemm_row_blocks(int M) { return M > 32 ? 2 : 1; }
 inline int gemm_col_blocks(bool a_f32) { return a_f32 ? 2 : 1; }
 hipError_t launch_cache_write_finish(const CacheWriteArgs& a, int tokens, hipStream_t s);
 hipError_t launch_query_finish(const QueryArgs& a, int tokens, hipStream_t s);
+// bf16 queries: q~_i = (W^UK_i)^T q^C_i straight from the K-split partials of q^C, and the
+// q^R finish, in one launch (d_h a multiple of 32, at most 256).
+hipError_t launch_query_absorb(const QueryArgs& a, int tokens, hipStream_t s);
 hipError_t launch_sum_partials(const float* part, int64_t part_ks, int ksplit, int64_t n, void* out, bool out_bf16,
                                hipStream_t s);
 hipError_t launch_transpose_heads(const void* src, void* dst, int heads, int rows, int cols, bool bf16_elems,

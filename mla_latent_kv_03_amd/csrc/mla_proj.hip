@@ -381,20 +381,9 @@ __device__ __forceinline__ f32x4 sum_partials4(const float* src, int64_t ks_stri
   return v;
 }
 
-__global__ __launch_bounds__(256) void query_finish(const QueryArgs a, int tokens, int c_blocks) {
-  const int64_t nc = (int64_t)tokens * a.n_h * a.d_h, nr = (int64_t)tokens * a.n_h * a.d_r;
-  if ((int)blockIdx.x < c_blocks) {
-    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (e0 >= nc) return;
-    const int n = (int)min((int64_t)4, nc - e0);
-    const f32x4 v = sum_partials4(a.part_c + e0, a.part_c_ks, a.ksplit, n);
-    if (n == 4 && (nc & 3) == 0) *(f32x4*)(a.q_c + e0) = v;
-    else
-      for (int k = 0; k < n; ++k) a.q_c[e0 + k] = v[k];
-    return;
-  }
-  const int64_t e0 = ((int64_t)(blockIdx.x - c_blocks) * 256 + threadIdx.x) * 4;
-  if (e0 >= nr) return;
+// q^R finish for n elements from e0 (4 per thread): sum of the K-split partials, then each
+// interleaved pair rotated by its token's position.
+__device__ __forceinline__ void finish_q_rope(const QueryArgs& a, int64_t e0, int64_t nr) {
   const int n = (int)min((int64_t)4, nr - e0);
   f32x4 v = sum_partials4(a.part_r + e0, a.part_r_ks, a.ksplit_r, n);
   const int per_tok = a.n_h * a.d_r;
@@ -412,6 +401,154 @@ __global__ __launch_bounds__(256) void query_finish(const QueryArgs a, int token
   for (int k = 0; k < n; ++k) {
     if (a.out_bf16) ((bf16*)a.q_pe)[e0 + k] = (bf16)v[k];
     else ((float*)a.q_pe)[e0 + k] = v[k];
+  }
+}
+
+__global__ __launch_bounds__(256) void query_finish(const QueryArgs a, int tokens, int c_blocks) {
+  const int64_t nc = (int64_t)tokens * a.n_h * a.d_h, nr = (int64_t)tokens * a.n_h * a.d_r;
+  if ((int)blockIdx.x < c_blocks) {
+    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e0 >= nc) return;
+    const int n = (int)min((int64_t)4, nc - e0);
+    const f32x4 v = sum_partials4(a.part_c + e0, a.part_c_ks, a.ksplit, n);
+    if (n == 4 && (nc & 3) == 0) *(f32x4*)(a.q_c + e0) = v;
+    else
+      for (int k = 0; k < n; ++k) a.q_c[e0 + k] = v[k];
+    return;
+  }
+  const int64_t e0 = ((int64_t)(blockIdx.x - c_blocks) * 256 + threadIdx.x) * 4;
+  if (e0 < nr) finish_q_rope(a, e0, nr);
+}
+
+// The absorption product of the bf16 query prologue, fused with the partial sums:
+// workgroup (head i, block of 64 tokens, block of 256 latent columns) sums the K-split
+// partials of its q^C rows in float32 (every load of the workgroup in flight together),
+// keeps them in LDS as a bf16 high part and remainder (the projections' float32 operand
+// form: two MFMAs per k-step), and each wave multiplies them by 64 rows of (W^UK_i)^T,
+// read straight from memory, on 32x32x16 MFMAs: q~_i[t][c] = sum_k q^C_i[t][k] W^UK_i[k][c].
+// Chunk c (16 bytes) of LDS row r sits at c ^ (r % 8) (r % 4 when d_h is an odd multiple
+// of 32: a row then holds a multiple of 4 chunks, not of 8), so the operand reads (one chunk
+// of 32 rows) spread over the banks.  The workgroups past the products finish q^R.
+constexpr int kQaTok = 64, kQaCols = 256, kQaMaxDh = 256;   // LDS: 64 rows x d_h x 4 bytes
+
+__global__ __launch_bounds__(256) void query_absorb(const QueryArgs a, int tokens, int n_prod) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char qa_lds[];
+  if ((int)blockIdx.x >= n_prod) {
+    const int64_t nr = (int64_t)tokens * a.n_h * a.d_r;
+    const int64_t e0 = ((int64_t)(blockIdx.x - n_prod) * 256 + threadIdx.x) * 4;
+    if (e0 < nr) finish_q_rope(a, e0, nr);
+    return;
+  }
+  const int d_h = a.d_h, d_c = a.d_c;
+  const int n_tb = (tokens + kQaTok - 1) / kQaTok, n_cb = (d_c + kQaCols - 1) / kQaCols;
+  const int head = (int)blockIdx.x / (n_tb * n_cb);
+  const int rest = (int)blockIdx.x - head * n_tb * n_cb;
+  const int t0 = (rest / n_cb) * kQaTok, c_blk = (rest % n_cb) * kQaCols;
+  const int row_bytes = d_h * 2;                           // one bf16 row of A
+  const int swz = d_h % 64 == 0 ? 7 : 3;
+  unsigned char* a_hi = qa_lds;
+  unsigned char* a_lo = qa_lds + kQaTok * row_bytes;
+
+  // Sum of the partials, 4 elements per thread and item, 8 items' loads in flight together
+  // (a loop of one item at a time would wait for each item's loads in turn); rows past the
+  // tokens are zero.
+  const int64_t stride_t = (int64_t)a.n_h * d_h;
+  const int per_row4 = d_h / 4, items = kQaTok * per_row4;
+  for (int q0 = threadIdx.x; q0 < items; q0 += 256 * 8) {
+    f32x4 v[8];
+    const float* src[8];
+    bool ok[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int q = q0 + 256 * u;
+      const int r = q / per_row4, k = (q - r * per_row4) * 4;
+      ok[u] = q < items && t0 + r < tokens;
+      src[u] = a.part_c + (ok[u] ? (t0 + r) * stride_t + (int64_t)head * d_h + k : 0);
+      v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int j = 0; j < a.ksplit; ++j) {             // K chunks in order, as the other finishers
+      f32x4 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = *(const f32x4*)(src[u] + (int64_t)j * a.part_c_ks);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (ok[u]) v[u] += x[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int q = q0 + 256 * u;
+      if (q >= items) break;
+      const int r = q / per_row4, k = (q - r * per_row4) * 4;
+      const bf16x4 hi = to_bf16x4(v[u]);
+      const bf16x4 lo = to_bf16x4(v[u] - from_bf16x4(hi));
+      const int off = r * row_bytes + 16 * ((k >> 3) ^ (r & swz)) + 2 * (k & 7);
+      *(bf16x4*)(a_hi + off) = hi;
+      *(bf16x4*)(a_lo + off) = lo;
+    }
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, kh = lane >> 5;
+  const int c0 = c_blk + 64 * wave;
+  if (c0 >= d_c) return;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[nb][mb][v] = 0.f;
+  // B rows of this lane: columns c0 + 32 nb + l32 of q~, i.e. rows of (W^UK_i)^T.
+  const bf16* wrow[2];
+  bool wok[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int c = c0 + 32 * nb + l32;
+    wok[nb] = c < d_c;
+    wrow[nb] = (const bf16*)a.w_uk_t + ((int64_t)head * d_c + (wok[nb] ? c : 0)) * d_h + 8 * kh;
+  }
+  for (int k0 = 0; k0 < d_h; k0 += 128) {
+    // Up to 8 k-steps of B at once (16 loads in flight per lane); steps past d_h load a
+    // valid fragment of the row (its last) and are not used.
+    bf16x8 w[8][2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const bf16x8 x = *(const bf16x8*)(wrow[nb] + min(k0 + 16 * j, d_h - 16));
+        w[j][nb] = wok[nb] ? x : bf16x8{};
+      }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + 16 * j;
+      if (k >= d_h) break;
+      const int chunk = (k >> 3) + kh;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int r = 32 * mb + l32;
+        const int off = r * row_bytes + 16 * (chunk ^ (r & swz));
+        const bf16x8 hi = *(const bf16x8*)(a_hi + off);
+        const bf16x8 lo = *(const bf16x8*)(a_lo + off);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, w[j][nb], acc[nb][mb], 0, 0, 0);
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, w[j][nb], acc[nb][mb], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // Lane holds q~[t0 + 32 mb + 8 (v/4) + 4 kh + v%4][c0 + 32 nb + l32].
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    if (!wok[nb]) continue;
+    const int c = c0 + 32 * nb + l32;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = t0 + 32 * mb + 8 * (v >> 2) + 4 * kh + (v & 3);
+        if (t < tokens) ((bf16*)a.q_nope)[((int64_t)t * a.n_h + head) * d_c + c] = (bf16)acc[nb][mb][v];
+      }
   }
 }
 
@@ -491,6 +628,16 @@ hipError_t launch_gemm_nt(const GemmArgs& g, bool bf16_operands, int ksplit, hip
 hipError_t launch_cache_write_finish(const CacheWriteArgs& a, int tokens, hipStream_t s) {
   const int waves = (a.d_c + a.d_r + 127) / 128;   // one thread per element pair
   hipLaunchKernelGGL(cache_write_finish, dim3(tokens), dim3(64 * waves), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_query_absorb(const QueryArgs& a, int tokens, hipStream_t s) {
+  if (a.d_h % 32 || a.d_h > kQaMaxDh || a.d_c < 1 || !a.out_bf16) return hipErrorInvalidValue;
+  const int n_prod = a.n_h * ((tokens + kQaTok - 1) / kQaTok) * ((a.d_c + kQaCols - 1) / kQaCols);
+  const int64_t nr = (int64_t)tokens * a.n_h * a.d_r;
+  const int r_blocks = (int)((nr + 1023) / 1024);
+  const size_t lds = (size_t)kQaTok * a.d_h * 4;          // bf16 high and low rows
+  hipLaunchKernelGGL(query_absorb, dim3(n_prod + r_blocks), dim3(256), lds, s, a, tokens, n_prod);
   return hipGetLastError();
 }
 

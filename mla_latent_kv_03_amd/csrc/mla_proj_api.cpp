@@ -250,7 +250,8 @@ mla_status_t mla_query_prologue(const mla_decode_params_t* params, int32_t d_mod
     st = status_of(mla::launch_gemm_nt(g, bf16, l.sr.ksplit, s));
     if (st != MLA_OK) return st;
   }
-  // Sum the partials; q^C to float32 scratch, q^R rotated to q_pe.
+  // Sum the partials; q^C to float32 scratch (or, bf16 queries, straight into the absorption
+  // product), q^R rotated to q_pe.
   mla::QueryArgs qa;
   qa.part_c = part_c;
   qa.part_r = part_r;
@@ -266,6 +267,13 @@ mla_status_t mla_query_prologue(const mla_decode_params_t* params, int32_t d_mod
   qa.q_pe = q_pe;
   qa.out_bf16 = bf16 ? 1 : 0;
   qa.rope_base = rope_base;
+  qa.w_uk_t = w_uk_t;
+  qa.q_nope = q_nope;
+  qa.d_c = p.d_c;
+  if (bf16 && d_h <= 256) {
+    // q~ from the partials of q^C directly, and q^R, in one launch.
+    return status_of(mla::launch_query_absorb(qa, T, s));
+  }
   st = status_of(mla::launch_query_finish(qa, T, s));
   if (st != MLA_OK) return st;
   // q~_i = (W^UK_i)^T q^C_i: per head, C[T, d_c] = q^C_i[T, d_h] ((W^UK_i)^T)^T, written

@@ -311,6 +311,36 @@ def test_query_prologue_ragged_k():
     record("query_prologue ragged K q_pe", *assert_close(to_np(qp), want_p, BF16_TOL, "q_pe"), n=want_p.size)
 
 
+@pytest.mark.parametrize("n_h,B,d_model,d_h,d_c,d_r", [(4, 37, 512, 64, 176, 16), (2, 65, 256, 256, 528, 32)])
+def test_query_prologue_token_and_column_edges(n_h, B, d_model, d_h, d_c, d_r):
+    """Absorption product at widths the V3 shape does not reach: 74 and 130 query rows (two and
+    three blocks of 64 tokens, the last one partial), latent widths 176 and 528 (blocks of 256
+    columns ending inside a wave's 64 columns and inside a 32-column block), and d_h 256 (two
+    rounds of eight k-steps).  q_nope and q_pe against the oracle."""
+    _case("query_prologue edges", n_h=n_h, B=B, d_h=d_h, d_c=d_c)
+    from mla_latent_kv_03_amd import binding
+    s_q = 2
+    w = workloads.layer_weights(1361 + d_h, d_model=d_model, n_h=n_h, d_c=d_c, d_h=d_h, d_r=d_r, d_v=16,
+                                n_tokens=B * s_q, with_o=False)
+    positions = np.random.default_rng(1362).integers(0, 131072, size=(B, s_q)).astype(np.int32)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16)
+    h = bf(w["h"]).reshape(B, s_q, d_model)
+    wq, wqr = bf(w["q"]), bf(w["qr"])
+    uk_t = bf(np.transpose(w["uk"], (0, 2, 1)))
+    params = binding.make_params(batch=B, s_q=s_q, n_h=n_h, d_c=d_c, d_r=d_r, d_v=16, page_size=64, num_pages=1,
+                                 max_pages_per_seq=1, c_kv_stride=d_c + d_r, k_pe_stride=d_c + d_r,
+                                 softmax_scale=1.0, q_dtype=binding.BF16, kv_dtype=binding.BF16)
+    qn, qp = binding.mla_query_prologue(params, h.cuda(), wq.cuda(), uk_t.cuda(), wqr.cuda(),
+                                        torch.from_numpy(positions).cuda(), d_h=d_h)
+    torch.cuda.synchronize()
+    want_n, want_p = ref.query_rows(h.double().numpy(), wq.double().numpy(), bf(w["uk"]).double().numpy(),
+                                    wqr.double().numpy(), positions)
+    record(f"query_prologue edges d_h={d_h} d_c={d_c} q_nope", *assert_close(to_np(qn), want_n, BF16_TOL, "q_nope"),
+           n=want_n.size)
+    record(f"query_prologue edges d_h={d_h} d_c={d_c} q_pe", *assert_close(to_np(qp), want_p, BF16_TOL, "q_pe"),
+           n=want_p.size)
+
+
 # ------------------------------------------------------------------ output projection and fold
 
 def test_output_projection_tiny_layer_f32_both_forms():
