@@ -144,6 +144,20 @@ __device__ __forceinline__ void score_mfma(f32x16& s, bf16x8 a, bf16x8 b) {
                : "+v"(s)
                : "v"(__builtin_bit_cast(u32x4v, a)), "v"(__builtin_bit_cast(u32x4v, b)));
 }
+// E4M3 scores: the E4M3 key rows times an E4M3 part of the queries, 32x32x64 with E8M0
+// block scales (scale_a for the keys: 1; scale_b: 1 for the queries' high part, 2^-4 for
+// the remainder part), into the same VGPR accumulator and with the same hazards as above.
+typedef unsigned u32x8v __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ void score8_first(f32x16& s, u32x8v a, u32x8v b, uint32_t sa, uint32_t sb) {
+  asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]"
+               : "=&v"(s)
+               : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+__device__ __forceinline__ void score8(f32x16& s, u32x8v a, u32x8v b, uint32_t sa, uint32_t sb) {
+  asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+v"(s)
+               : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
 __device__ __forceinline__ void scores_ready(f32x16& s) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
 }
@@ -381,6 +395,48 @@ void attn_partial_h128(const AttnParams p) {
           qf[ks] = *(const bf16x8*)(prow + 16u * (c ^ ((l32 >> 1) & 7u)));
       }
     };
+    // E4M3: the queries as two E4M3 parts with one power-of-two scale 2^k per head, the B
+    // operands of the scaled 32x32x64 MFMA: 2^k q = hi + lo / 16 exactly.  A bf16 value has
+    // 8 significant bits; hi keeps the first 4 (nearest), and the remainder is a multiple of
+    // the value's last bf16 step with at most 4 significant bits, so 16 times it is an E4M3
+    // value too (k puts the head's largest element below 2^8; elements more than 15 binades
+    // below it would lose bits and weigh less than 2^-15 of it).  The factor 2^-k of the
+    // head's scores goes into the lane's softmax scale.  Byte j of k-block kb's operand is
+    // the same dimension as byte j of the key operand: k-steps 4 kb .. 4 kb + 3 of qf in
+    // order (which matches two consecutive score reads of the tile).
+    u32x8v qh[kQk / 4], ql[kQk / 4];
+    float qs = p.scale_log2;      // the lane's scores to base-2 logits (E4M3: times 2^-k)
+    auto convert_queries = [&]() {
+      float amax = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kQk; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)qf[ks][j]));
+      amax = max_xor32(amax);                        // both lane halves hold the head's row
+      const int k = amax > 0.f ? 8 - __builtin_amdgcn_frexp_expf(amax) : 0;
+      qs = ldexpf(p.scale_log2, -k);
+#pragma unroll
+      for (int kb = 0; kb < kQk / 4; ++kb)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const bf16x8 src = qf[4 * kb + d / 2];
+          float x[4], r[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = ldexpf((float)src[4 * (d % 2) + i], k);
+          int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+          hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hi, true);
+          const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+          const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+          r[0] = (x[0] - b01[0]) * 16.f;
+          r[1] = (x[1] - b01[1]) * 16.f;
+          r[2] = (x[2] - b23[0]) * 16.f;
+          r[3] = (x[3] - b23[1]) * 16.f;
+          int lo = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+          lo = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], lo, true);
+          qh[kb][d] = (uint32_t)hi;
+          ql[kb][d] = (uint32_t)lo;
+        }
+    };
     const int tiles_per_page = p.page_size / kT;
     const uint32_t c_row = (uint32_t)p.c_stride * (FP8 ? 1u : 2u), k_row = (uint32_t)p.k_stride * (FP8 ? 1u : 2u);
 
@@ -566,6 +622,9 @@ void attn_partial_h128(const AttnParams p) {
       if (first_pass && !(first_piece && pc.b == b_guess)) load_queries();
 #pragma unroll
       for (int j = 0; j < LT::kCopies; ++j) copy_row(tc1, j, lz0);
+      if constexpr (FP8) {
+        if (first_pass) convert_queries();           // waits for the query loads (and tile 0)
+      }
       int vs = 0, ks3 = 0;   // ring slots of tile `it`
       for (int it = 0; it <= ntiles; ++it) {
         wait_copies();             // this wave's copies of tile `it` have landed, it+1's in flight
@@ -636,8 +695,7 @@ void attn_partial_h128(const AttnParams p) {
         // one wave per SIMD the reads' latency has to hide behind this wave's own MFMAs.
         f32x16 s;
         bf16x8 kq[kKPf + 1], va[4], pb[2][4];
-        u32x4 kr[2];          // E4M3: raw score operands, pair p in kr[p % 2], read two steps ahead
-        bf16x8 kop[2];        // E4M3: halves of the next pair, widened exactly one pair ahead of use
+        u32x8v k8[3];         // E4M3: key operand of k-block kb in k8[kb % 3], read two k-blocks ahead
         u32x2 vr[4];          // E4M3: value reads not yet widened
         f32x4 tsc[4];         // E4M3: per-token scales of tile `it` (read before the score chain ends)
         if constexpr (!FP8) {
@@ -645,11 +703,9 @@ void attn_partial_h128(const AttnParams p) {
           for (int j = 0; j < kKPf; ++j) kq[j] = kfrag(j);
           va[0] = vfrag(0, 0);
         } else {
-          kr[0] = kraw(0);
-          kr[1] = kraw(1);
+          k8[0] = __builtin_shufflevector(kraw(0), kraw(1), 0, 1, 2, 3, 4, 5, 6, 7);
+          k8[1] = __builtin_shufflevector(kraw(2), kraw(3), 0, 1, 2, 3, 4, 5, 6, 7);
           vr[0] = vraw8(0, 0);                       // widened at ks = 1, first used at ks = 3
-          kop[0] = e4m3x8_to_bf16(kr[0][0], kr[0][1]);
-          kop[1] = e4m3x8_to_bf16(kr[0][2], kr[0][3]);
         }
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) pb[0][hb] = pfrag(hb, 0);
@@ -702,25 +758,32 @@ void attn_partial_h128(const AttnParams p) {
           if (ks >= 30 && ks < 34) pb[1][ks - 30] = pfrag(ks - 30, 1);
           if (!FP8 && ks % 4 == 1) copy_row(tn, ks / 4, lo.ln);                     // ks = 1, 5, .., 33
           if (FP8 && ks % 8 == 1) copy_row(tn, ks / 8, lo.ln);                      // ks = 1, 9, .., 33
-          const bf16x8 ka = FP8 ? kop[ks % 2] : kq[ks % (kKPf + 1)];
-          if (ks == 0)
-            score_mfma_first(s, ka, qf[ks]);
-          else
-            score_mfma(s, ka, qf[ks]);
-          if constexpr (FP8) {
-            // After step ks's MFMA (pair p = ks / 2): the same half of pair p + 1, read two
-            // steps ago, is widened into the register step ks used; at the pair's first step
-            // pair p + 2 is read into the slot that pair p has left.
-            const int pn = ks / 2 + 1;
-            if (pn < kQk / 2) {
-              const u32x4 r = kr[pn % 2];
-              kop[ks % 2] = ks % 2 == 0 ? e4m3x8_to_bf16(r[0], r[1]) : e4m3x8_to_bf16(r[2], r[3]);
-            }
-            if (ks % 2 == 0 && pn + 1 < kQk / 2) kr[(pn + 1) % 2] = kraw(pn + 1);
+          if constexpr (!FP8) {
+            const bf16x8 ka = kq[ks % (kKPf + 1)];
+            if (ks == 0)
+              score_mfma_first(s, ka, qf[ks]);
+            else
+              score_mfma(s, ka, qf[ks]);
+          } else if (ks % 2 == 0) {
+            // Score MFMA j = ks / 2 (the even k-steps; the accumulation MFMAs take the odd
+            // ones): k-block j / 2, the queries' high part (j even, B scale 1) or remainder
+            // (j odd, B scale 2^-4).  After the high part's MFMA, k-block kb + 2 is read into
+            // the slot that k-block kb - 1 left.
+            const int j = ks / 2, kb = j / 2;
+            const uint32_t one = 127u, sixteenth = 123u;   // E8M0 exponents of 1 and 2^-4
+            if (j == 0)
+              score8_first(s, k8[0], qh[0], one, one);
+            else
+              score8(s, k8[kb % 3], j % 2 == 0 ? qh[kb] : ql[kb], one, j % 2 == 0 ? one : sixteenth);
+            if (j % 2 == 0 && kb + 2 < kQk / 4)
+              k8[(kb + 2) % 3] = __builtin_shufflevector(kraw(2 * kb + 4), kraw(2 * kb + 5), 0, 1, 2, 3, 4, 5, 6, 7);
           }
           if (ks >= 3 && ks % 2 == 1 && ks < 35) {
             const int a = (ks - 3) / 2;
             acc[a] = mfma32(va[a / 4], pb[0][a % 4], acc[a]);
+            // E4M3: pinned between the score MFMAs around it (the compiler otherwise sinks
+            // these MFMAs, which have no side effects, below the whole score chain).
+            if constexpr (FP8) asm volatile("" : "+a"(acc[a]));
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -751,7 +814,7 @@ void attn_partial_h128(const AttnParams p) {
           float mx = s[0];
 #pragma unroll
           for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-          m_ref = max_xor32(mx) * p.scale_log2;
+          m_ref = max_xor32(mx) * qs;
         }
         __builtin_amdgcn_sched_barrier(0);
         const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
@@ -798,7 +861,7 @@ void attn_partial_h128(const AttnParams p) {
           if (g < 4) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              x[4 * g + j] = __builtin_fmaf(s[4 * g + j], p.scale_log2, nm);
+              x[4 * g + j] = __builtin_fmaf(s[4 * g + j], qs, nm);
               if constexpr (FP8) rs[4 * g + j] = fminf(__builtin_amdgcn_rcpf(tsc[g][j]), 3.0e38f);
             }
           } else if (g < 12) {

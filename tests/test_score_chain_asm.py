@@ -2,7 +2,8 @@
 accumulator is touched by nothing but the chain's own MFMAs until the wait states that
 follow its last MFMA.
 
-The chain is written in inline assembly (its accumulator lives in VGPRs), so the
+The chain (bf16: 32x32x16; E4M3: scaled 32x32x64) is written in inline assembly (its
+accumulator lives in VGPRs), so the
 compiler does not know when an MFMA's result is written and inserts no wait for it.  A
 register copy that the compiler places between two chain MFMAs, or right after the last
 one, would read a result that is still being computed, and the output would depend on
@@ -37,7 +38,7 @@ def chain_violations(asm_lines):
     in a loop laid out with its head inside the chain, at the first in-place one), stays
     open through in-place MFMAs on the same registers, and closes after three
     `s_nop 7` (the wait before the result is read) or at an unconditional branch."""
-    mfma = re.compile(r"v_mfma_f32_32x32x16_bf16 v\[(\d+):(\d+)\], \S+, \S+, (\S+)")
+    mfma = re.compile(r"v_mfma_(?:f32_32x32x16_bf16|scale_f32_32x32x64_f8f6f4) v\[(\d+):(\d+)\], \S+, \S+, ([^,\s]+)")
     chains, bad, acc, nops = 0, [], None, 0
     for ln, line in enumerate(asm_lines, 1):
         t = line.split(";")[0].strip()
@@ -87,7 +88,8 @@ def asm():
 
 def test_score_chain_accumulator_untouched_until_its_wait(asm):
     chains, bad = chain_violations(asm)
-    # two kernels (bf16, E4M3), each with the first pass and the exact re-run
+    # two kernels (bf16 32x32x16, E4M3 scaled 32x32x64), each with the first pass and the
+    # exact re-run
     assert chains >= 4, f"expected the score chains of both kernels, found {chains}"
     assert not bad, "instructions touch an open score chain's accumulator:\n" + "\n".join(f"{ln}: {t}" for ln, t in bad[:10])
 
