@@ -285,6 +285,7 @@ def cpu_baseline(x, budget_s=12.0):
 
 
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+MFMA_F8_COUNTER = "SQ_INSTS_VALU_MFMA_MOPS_F8"   # optional: the E4M3 kernel's score MFMAs
 
 
 def pmc_summary(args):
@@ -294,7 +295,8 @@ def pmc_summary(args):
     SQ_INSTS_VALU_MFMA_MOPS_BF16 for the attention kernel, the record also gets the matrix unit's busy
     fraction (busy cycles summed over all SIMDs / (active cycles per XCD x SIMDs); the database holds
     GRBM_GUI_ACTIVE summed over the XCDs) and the counted bf16 MFMA flops (512 per MOP), medians
-    over the dispatches."""
+    over the dispatches; with SQ_INSTS_VALU_MFMA_MOPS_F8 as well, the E4M3 MFMA flops are counted the
+    same way and added."""
     import sqlite3
     kname, ksrc = attn_kernel(make_workload(args.workload))
     vals = {}   # (kernel kind, counter) -> per-dispatch totals
@@ -306,7 +308,7 @@ def pmc_summary(args):
         for r in db.execute("select * from counters_collection"):
             name, ctr = r[ci["kernel_name"]], r[ci["counter_name"]]
             kind = "attn" if kname in name else ("copy" if "neg_kernel" in name else None)
-            if kind is None or ctr not in ("FETCH_SIZE", "WRITE_SIZE") + MFMA_COUNTERS:
+            if kind is None or ctr not in ("FETCH_SIZE", "WRITE_SIZE", MFMA_F8_COUNTER) + MFMA_COUNTERS:
                 continue
             key = (kind, ctr, path, r[ci["dispatch_id"]])
             per[key] = per.get(key, 0.0) + float(r[ci["value"]])
@@ -332,6 +334,10 @@ def pmc_summary(args):
         frac = [b / (a / MI355X_XCDS * MI355X_SIMDS) for b, a in zip(busy, active)]
         rec["mfma_busy_frac"] = round(statistics.median(frac), 4)
         rec["mfma_counted_flops"] = round(statistics.median(mops) * 512)
+        if ("attn", MFMA_F8_COUNTER) in vals:
+            rec["mfma_counted_flops_bf16"] = rec["mfma_counted_flops"]
+            rec["mfma_counted_flops_f8"] = round(statistics.median(vals[("attn", MFMA_F8_COUNTER)]) * 512)
+            rec["mfma_counted_flops"] += rec["mfma_counted_flops_f8"]
         print(f"workload {args.workload}: MFMA busy {rec['mfma_busy_frac']:.1%} of active SIMD cycles, "
               f"{rec['mfma_counted_flops'] / 1e9:.2f} GFLOP counted per launch")
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
