@@ -51,11 +51,12 @@
 //
 // E4M3 caches (page "MLA deep compression" gives the cache bytes per token as the lever;
 // one fp32 scale per token, value = code * scale): the same pipeline on tiles of 512 +
-// 64 bytes per token plus the scales, at half the copies.  A 128-bit score read gives 16
-// values, the operands of two MFMA k-steps (the queries are loaded in the same k order);
-// a transposed 8-bit read gives a whole 8-token value operand.  Both are widened to bf16
-// exactly; the token scales multiply the scores and the probabilities (rounded to bf16
-// afterwards), which is the dequantized attention.
+// 64 bytes per token plus the scales, at half the copies.  The scores run on the matrix
+// unit's E4M3 path (scaled 32x32x64 MFMAs): two 128-bit reads give a lane 32 key values as
+// stored, and the bf16 queries enter as two E4M3 parts that represent them exactly (below).
+// A transposed 8-bit read gives a whole 8-token value operand, widened to bf16 exactly for
+// the accumulation.  The token scales multiply the scores and the probabilities (rounded
+// to bf16 afterwards), which is the dequantized attention.
 
 #include "mla_device.h"
 #include "mla_kernels.h"
@@ -793,8 +794,8 @@ void attn_partial_h128(const AttnParams p) {
         // are masked.
         scores_ready(s);
         // E4M3: the per-token scales of tile `it` for this lane's tokens 8 g + 4h + i; the
-        // key rows were widened without them, so they multiply the scores here and the
-        // probabilities below (value rows).
+        // key rows entered the score MFMAs without them, so they multiply the scores here and
+        // the probabilities below (value rows).
         if constexpr (FP8) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) s[v] *= tsc[v >> 2][v & 3];
