@@ -115,6 +115,8 @@ struct Smem {
   int redo[kWaves];                           // per wave: a tile exceeded the reference maximum
 };
 static_assert(sizeof(Smem<false>) <= 160 * 1024 && sizeof(Smem<true>) <= 160 * 1024, "LDS budget of one workgroup");
+// The bf16 score reads address the RoPE ring as the bytes right after the value ring.
+static_assert(offsetof(Smem<false>, k) == kVRing * kVTile, "RoPE ring follows the value ring");
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   // C[32x32] += A[32x16] B[16x32]: lane l holds A[l%32][8(l/32) + j], B[8(l/32) + j][l%32]
