@@ -45,6 +45,9 @@ def attn_kernel(x):
     return "attn_partial_split", ("mla_attn_mfma.hip", "mla_device.h", "mla_split.h")
 
 
+COMBINE_SRC = ("mla_combine.hip", "mla_device.h", "mla_kernels.h")
+
+
 def source_digest(files):
     import hashlib
     h = hashlib.sha256()
@@ -296,7 +299,9 @@ def pmc_summary(args):
     fraction (busy cycles summed over all SIMDs / (active cycles per XCD x SIMDs); the database holds
     GRBM_GUI_ACTIVE summed over the XCDs) and the counted bf16 MFMA flops (512 per MOP), medians
     over the dispatches; with SQ_INSTS_VALU_MFMA_MOPS_F8 as well, the E4M3 MFMA flops are counted the
-    same way and added."""
+    same way and added.  FETCH_SIZE / WRITE_SIZE of the combine kernel (same runs, same scaling) give
+    the whole step's traffic per call, attention plus combine, recorded with the combine's own source
+    digest.  The E4M3 step's separate append launch (a few new rows) is not counted."""
     import sqlite3
     kname, ksrc = attn_kernel(make_workload(args.workload))
     vals = {}   # (kernel kind, counter) -> per-dispatch totals
@@ -307,7 +312,8 @@ def pmc_summary(args):
         per = {}
         for r in db.execute("select * from counters_collection"):
             name, ctr = r[ci["kernel_name"]], r[ci["counter_name"]]
-            kind = "attn" if kname in name else ("copy" if "neg_kernel" in name else None)
+            kind = ("attn" if kname in name else "copy" if "neg_kernel" in name
+                    else "comb" if "combine_upproj" in name else None)
             if kind is None or ctr not in ("FETCH_SIZE", "WRITE_SIZE", MFMA_F8_COUNTER) + MFMA_COUNTERS:
                 continue
             key = (kind, ctr, path, r[ci["dispatch_id"]])
@@ -328,6 +334,12 @@ def pmc_summary(args):
            "copy_factor_fetch": round(f_read, 4), "copy_factor_write": round(f_write, 4),
            "attn_dispatches": len(vals[("attn", "FETCH_SIZE")]), "command": args.pmc_command,
            "kernel": kname, "source_digest": source_digest(ksrc)}
+    if ("comb", "FETCH_SIZE") in vals and ("comb", "WRITE_SIZE") in vals:
+        c_fetch = mean[("comb", "FETCH_SIZE")] * 1024 / f_read
+        c_write = mean[("comb", "WRITE_SIZE")] * 1024 / f_write
+        rec.update({"combine_fetch_bytes": round(c_fetch), "combine_write_bytes": round(c_write),
+                    "combine_source_digest": source_digest(COMBINE_SRC),
+                    "step_bytes_per_launch": round(fetch + write + c_fetch + c_write)})
     if all(("attn", c) in vals for c in MFMA_COUNTERS):
         import statistics
         busy, active, mops = (vals[("attn", c)] for c in MFMA_COUNTERS)
@@ -344,6 +356,10 @@ def pmc_summary(args):
     data = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
     data[args.workload] = rec
     json.dump(data, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
+    if "step_bytes_per_launch" in rec:
+        print(f"workload {args.workload}: combine kernel HBM traffic per launch "
+              f"{(rec['combine_fetch_bytes'] + rec['combine_write_bytes']) / 1e6:.1f} MB; whole step "
+              f"{rec['step_bytes_per_launch'] / 1e6:.1f} MB")
     print(f"workload {args.workload}: attention kernel HBM traffic per launch {rec['bytes_per_launch'] / 1e6:.1f} MB "
           f"(fetch {fetch / 1e6:.1f} MB, write {write / 1e6:.1f} MB); copy calibration: FETCH_SIZE reads "
           f"{f_read:.4f}x and WRITE_SIZE {f_write:.4f}x the {args.copy_calibration_mb} MiB copied; "
@@ -614,6 +630,12 @@ def main():
             counted["traffic_gbs"] = round(traffic / (attn_ms * 1e-3) / 1e9, 1)
             if "mfma_busy_frac" in rec:
                 counted["mfma_busy_frac_counter"] = rec["mfma_busy_frac"]
+            # Whole step (attention + combine launches) against the step's algorithmic bytes
+            # (cache and queries once, W^UV once), if the combine is the one the counters saw.
+            if "step_bytes_per_launch" in rec and rec.get("combine_source_digest") == source_digest(COMBINE_SRC):
+                counted["step_traffic"] = rec["step_bytes_per_launch"]
+                counted["step_algorithmic_bytes"] = alg["total_bytes"]
+                counted["step_traffic_ratio"] = round(rec["step_bytes_per_launch"] / alg["total_bytes"], 4)
     peaks = None if args.no_peaks else measured_peaks(dev)
     if peaks:
         print(f"[bench] measured peaks: HBM read {peaks['hbm_read_gbs']:.0f} GB/s, bf16 MFMA "
